@@ -1,0 +1,185 @@
+"""Benchmark of one Muon step (momentum -> batched Newton-Schulz -> decoupled
+weight decay) on one MI355X, through the C ABI.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+
+Prints ONE JSON line.  A step is one muon_step call over the whole parameter
+set of the workload, with inputs (weights, gradients, momenta) resident in
+HBM before timing starts; gradient sets are drawn beforehand and cycled.
+`value` is the algorithmic NS throughput in TFLOP/s (3*m^2*n + m^3 flops per
+matrix per NS iteration, m <= n).  `roofline` reports the dominant kernel
+against its bound, and `cpu_baseline` the fp64 CPU oracle on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
+
+
+def alg_flops(wl) -> float:
+    """3 m^2 n + m^3 per matrix per NS iteration (Gram exploits symmetry)."""
+    tot = 0.0
+    for s in wl.shapes:
+        b = s[0] if len(s) == 3 else 1
+        r, c = s[-2], s[-1]
+        m, n = min(r, c), max(r, c)
+        tot += b * (3.0 * m * m * n + float(m) ** 3)
+    return tot * wl.ns_steps
+
+
+def alg_bytes(wl) -> float:
+    """Compulsory HBM bytes of a step: read G, M, W; write M, W."""
+    import torch
+    pes = 2 if wl.dtype == torch.bfloat16 else 4
+    return wl.n_elements() * (pes + 4 + 4 + pes + pes)
+
+
+def cpu_baseline(wl, budget_s: float):
+    """Time the fp64 oracle on host cores over a bounded sample of the workload."""
+    import numpy as np
+    import torch
+
+    from oracle import muon_ref as ref
+    from newton_schulz_05_amd import workloads as WL
+
+    a, b, c = wl.coeffs
+    hp = ref.MuonHyper(lr=wl.lr, mu=wl.mu, nesterov=wl.nesterov, wd=wl.wd, a=a, b=b, c=c,
+                       ns_steps=wl.ns_steps, scale=wl.scale)
+    params = WL.make_params(wl, "cpu")
+    grads = WL.make_grads(wl, 0, "cpu")
+    w = [p.double().numpy() for p in params]
+    g = [x.double().numpy() for x in grads]
+    mo = [np.zeros(x.shape) for x in w]
+    # sample: whole parameters in order until the time budget is spent
+    flops_done, t0, n_params = 0.0, time.perf_counter(), 0
+    i = 0
+    while time.perf_counter() - t0 < budget_s:
+        k = i % len(w)
+        ref.muon_step([w[k]], [g[k]], [mo[k]], hp)
+        sub = type(wl)(wl.key, wl.number, wl.name, (wl.shapes[k],), wl.dtype, wl.g_std)
+        flops_done += alg_flops(sub)
+        i += 1
+        n_params += 1
+    el = time.perf_counter() - t0
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([x.get("num_threads", 1) for x in info] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    return {"value": flops_done / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_params} parameter-steps of {wl.name} (fp64 NumPy, {el:.1f} s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path: every GPU would run its own shard's step independently)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from newton_schulz_05_amd import MuonPlan
+    from newton_schulz_05_amd import workloads as WL
+
+    wl = WL.WORKLOADS[args.config]
+    big = args.config in ("c4", "c5")
+    steps = args.steps if args.steps is not None else (10 if big else 100)
+    warmup = args.warmup if args.warmup is not None else (2 if big else 10)
+    dev = "cuda"
+    plan = MuonPlan(wl.shapes, wl.dtype)
+    ws = plan.new_workspace(dev)
+    params = WL.make_params(wl, dev, dev)
+    moms = WL.make_moms(wl, dev)
+    n_sets = 2 if big else 4
+    gsets = [WL.make_grads(wl, s, dev, dev) for s in range(n_sets)]
+    torch.cuda.synchronize()
+    hyper = wl.hyper()
+    stream = torch.cuda.current_stream()
+
+    for s in range(warmup):
+        plan.step(params, gsets[s % n_sets], moms, **hyper, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+
+    # per-step HIP events on the stream the kernels are launched on
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for s in range(steps):
+        plan.step(params, gsets[s % n_sets], moms, **hyper, workspace=ws, stream=stream)
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    ms = sum(per) / steps
+    flops = alg_flops(wl)
+    byt = alg_bytes(wl)
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    groups = plan.groups()
+    skinny_only = all(g["m"] <= 32 for g in groups) and wl.dtype == torch.bfloat16
+    if skinny_only:
+        # one persistent kernel per chunk; with one chunk the step is one launch
+        gbs = byt / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "skinny_kernel", "launches_per_step": sum(g["n_chunks"] for g in groups)}
+    elif wl.dtype == torch.bfloat16:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "whole step"}
+    else:
+        roof = {"bound": "alu", "achieved": round(tflops, 3), "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / F32_VALU_PEAK_TFLOPS, 6), "traffic": None, "kernel": "whole step"}
+
+    out = {
+        "metric": "Muon step ms & TFLOP/s (% bf16 MFMA peak / % HBM BW) for batched NS on [B,M,N]",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "ms_per_step_min": round(min(per), 5),
+        "wall_s": round(wall, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "matrices": wl.n_matrices(), "elements": wl.n_elements(),
+                   "ns_steps": wl.ns_steps, "alg_tflop_per_step": flops / 1e12,
+                   "compulsory_gb_per_step": byt / 1e9, "hbm_gbs_compulsory": round(byt / (ms * 1e-3) / 1e9, 1),
+                   "parallelism": "single_gpu"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl if not big else WL.custom([wl.shapes[0]], dtype=wl.dtype,
+                                                                        g_std=wl.g_std, number=wl.number),
+                                           args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,143 @@
+/*
+ * muon.h - C ABI of the MI355X (gfx950) Muon optimizer step library.
+ *
+ * One Muon step, as described by the HyperParallel FSDP Muon optimizer
+ * performance RFC (mindspore-ai/hyper-parallel):
+ *   - item 1(1): Newton-Schulz (NS) orthogonalisation runs on the gradient
+ *     momentum M_t and needs every matrix whole;
+ *   - item 2:    a 3-D expert slab [E, M, N] is E independent matrices;
+ *   - item 3:    matrices with the same trailing [M, N] shape are processed
+ *                together as one batch [B, M, N] (kernel fusion), which cuts
+ *                host dispatch, small allocations and synchronisation;
+ *   - item 6:    an AdamW-style decoupled weight decay term joins the update.
+ * The RFC gives no formula.  The library computes, per matrix (the readings
+ * are documented with the oracle):
+ *     M   <- mu*M + G
+ *     U    = G + mu*M   (nesterov != 0)   or   U = M
+ *     X0   = U / (||U||_F + 1e-7), transposed to wide (rows <= cols) if tall
+ *     X   <- a*X + (b*A + c*A^2)*X  with A = X*X^T, ns_steps times
+ *     O    = X (transposed back if the parameter is tall)
+ *     W   <- W - lr*(scale*O + wd*W)
+ *
+ * Conventions for every entry point:
+ *   - Device buffers (params, grads, momenta, outputs, workspace) belong to
+ *     the caller.  The step entry points allocate and free nothing on the
+ *     device and never synchronise the host with the device; they enqueue
+ *     work on `stream` (a hipStream_t passed as void*, NULL = null stream)
+ *     and return.
+ *   - Pointer arguments named `*_ptrs` are HOST arrays of DEVICE pointers,
+ *     one per parameter, in plan order.
+ *   - Every tensor is dense row-major [batch, rows, cols], 16-byte aligned,
+ *     and no two tensors overlap.
+ *   - Arguments are validated before anything is enqueued.  A non-OK status
+ *     from validation leaves every buffer untouched.  MUON_ERR_HIP means a
+ *     launch failed after work may have been enqueued: buffer contents are
+ *     then unspecified.
+ *   - muon_last_error_detail() gives a thread-local text for the last error.
+ *   - A plan holds only host metadata; it may be used from several host
+ *     threads one call at a time.  Two calls that share a workspace must be
+ *     ordered on one stream (the workspace holds per-call state).
+ */
+#ifndef MUON_H
+#define MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = 1,   /* null pointer, bad count, bad scalar */
+  MUON_ERR_SHAPE = 2,         /* a dimension < 1, or shapes do not match the plan */
+  MUON_ERR_DTYPE = 3,         /* dtype combination not supported */
+  MUON_ERR_PLAN_MISMATCH = 4, /* n_params or shapes differ from the plan's */
+  MUON_ERR_WORKSPACE = 5,     /* workspace null, too small or misaligned */
+  MUON_ERR_HIP = 6,           /* a HIP runtime call or kernel launch failed */
+  MUON_ERR_ALIGNMENT = 7      /* a tensor pointer is not 16-byte aligned */
+} muon_status;
+
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
+
+/* Shape of one parameter.  A 2-D matrix [rows, cols] has batch = 1; an expert
+ * slab [E, rows, cols] has batch = E and is E independent matrices (RFC item 2). */
+typedef struct {
+  int64_t batch;
+  int64_t rows;
+  int64_t cols;
+} muon_shape;
+
+typedef struct muon_plan_s* muon_plan;
+
+/* Build a plan for a fixed list of parameter shapes (RFC item 3: group by the
+ * trailing shape).  Host only; no device work.
+ *   shapes    : host array of n_params shapes (copied).
+ *   n_params  : >= 1.
+ *   param_dt  : dtype of params and grads (MUON_F32 or MUON_BF16).  The NS
+ *               arithmetic follows it: fp32 params get an fp32 NS, bf16
+ *               params the bf16-MFMA recipe with fp32 accumulation.
+ *   grad_dt   : must equal param_dt.
+ *   mom_dt    : dtype of the momenta; MUON_F32 only.
+ *   out       : receives the plan.
+ * Matrices are grouped by (min(rows,cols), max(rows,cols)); tall matrices
+ * (rows > cols) join the group of their transpose and are handled in the wide
+ * orientation.  The device is queried once, for its compute-unit count. */
+muon_status muon_plan_create(const muon_shape* shapes, int32_t n_params, muon_dtype param_dt,
+                             muon_dtype grad_dt, muon_dtype mom_dt, muon_plan* out);
+
+void muon_plan_destroy(muon_plan plan);
+
+/* Bytes of device workspace muon_step / muon_ns need for this plan. */
+muon_status muon_plan_workspace_bytes(muon_plan plan, size_t* bytes);
+
+/* Number of shape groups, and for group g: canonical (m, n) = (min, max),
+ * the number of matrices, how many of them are stored tall, and the number
+ * of launches ("chunks") the group is split into. */
+muon_status muon_plan_num_groups(muon_plan plan, int32_t* n_groups);
+muon_status muon_plan_group_info(muon_plan plan, int32_t g, int64_t* m, int64_t* n,
+                                 int64_t* count, int64_t* n_transposed, int64_t* n_chunks);
+
+/* The workspace must be zero-filled once before its first use with any plan
+ * (a small region of it holds cross-workgroup barrier counters that every
+ * completed call leaves at zero). */
+
+/* One Muon step on every parameter of the plan (see the formulas above).
+ *   param_ptrs : W, updated in place, dtype param_dt.
+ *   grad_ptrs  : G, read only, dtype grad_dt.
+ *   mom_ptrs   : M, updated in place, fp32.
+ *   shapes     : must equal the plan's shapes (checked).
+ *   lr, wd, scale, mu : finite; mu in [0, 1); nesterov 0 or 1.
+ *   a, b, c    : NS polynomial coefficients, finite.
+ *   ns_steps   : 0 .. 16.
+ *   workspace  : device buffer of at least muon_plan_workspace_bytes(),
+ *                256-byte aligned, zero-filled once before first use.
+ * Tensor results do not depend on how matrices are grouped or batched:
+ * every matrix is computed with the same tiling and reduction order
+ * whatever its batch, position or group. */
+muon_status muon_step(muon_plan plan, void* const* param_ptrs, const void* const* grad_ptrs,
+                      void* const* mom_ptrs, const muon_shape* shapes, int32_t n_params,
+                      float lr, float mu, int32_t nesterov, float wd, float a, float b,
+                      float c, int32_t ns_steps, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* NS alone: out = NS(in) for every parameter, in fp32, same shapes as in.
+ *   in_ptrs  : dtype param_dt (the NS input, e.g. a momentum), read only.
+ *   out_ptrs : fp32 outputs.
+ * Uses the same kernels and arithmetic as muon_step's NS. */
+muon_status muon_ns(muon_plan plan, const void* const* in_ptrs, float* const* out_ptrs,
+                    const muon_shape* shapes, int32_t n_params, float a, float b, float c,
+                    int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream);
+
+const char* muon_status_str(muon_status s);
+const char* muon_last_error_detail(void);
+
+/* Library version as an integer (major*10000 + minor*100 + patch). */
+int32_t muon_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H */

@@ -1,0 +1,222 @@
+"""ctypes binding of libmuon_hip.so (include/muon.h).
+
+Argument marshalling only: every step of the Muon update runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the stream.
+If the library has not been built the first call raises
+``MuonLibraryMissing``; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmuon_hip.so")
+
+MUON_F32 = 0
+MUON_BF16 = 1
+
+STATUS = {
+    0: "MUON_OK",
+    1: "MUON_ERR_INVALID_ARG",
+    2: "MUON_ERR_SHAPE",
+    3: "MUON_ERR_DTYPE",
+    4: "MUON_ERR_PLAN_MISMATCH",
+    5: "MUON_ERR_WORKSPACE",
+    6: "MUON_ERR_HIP",
+    7: "MUON_ERR_ALIGNMENT",
+}
+
+EXPORTS = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes",
+           "muon_plan_num_groups", "muon_plan_group_info", "muon_step", "muon_ns",
+           "muon_status_str", "muon_last_error_detail", "muon_version"]
+
+
+class MuonLibraryMissing(RuntimeError):
+    pass
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        self.detail = detail
+        super().__init__(f"{self.name}: {detail}")
+
+
+class MuonShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library once; raise MuonLibraryMissing if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise MuonLibraryMissing(
+            f"{path} not found: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32, i64, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    P = ctypes.POINTER
+    lib.muon_plan_create.argtypes = [P(MuonShape), i32, i32, i32, i32, P(vp)]
+    lib.muon_plan_create.restype = i32
+    lib.muon_plan_destroy.argtypes = [vp]
+    lib.muon_plan_destroy.restype = None
+    lib.muon_plan_workspace_bytes.argtypes = [vp, P(sz)]
+    lib.muon_plan_workspace_bytes.restype = i32
+    lib.muon_plan_num_groups.argtypes = [vp, P(i32)]
+    lib.muon_plan_num_groups.restype = i32
+    lib.muon_plan_group_info.argtypes = [vp, i32, P(i64), P(i64), P(i64), P(i64), P(i64)]
+    lib.muon_plan_group_info.restype = i32
+    lib.muon_step.argtypes = [vp, P(vp), P(vp), P(vp), P(MuonShape), i32, f32, f32, i32, f32,
+                              f32, f32, f32, i32, f32, vp, sz, vp]
+    lib.muon_step.restype = i32
+    lib.muon_ns.argtypes = [vp, P(vp), P(vp), P(MuonShape), i32, f32, f32, f32, i32, vp, sz, vp]
+    lib.muon_ns.restype = i32
+    lib.muon_status_str.argtypes = [i32]
+    lib.muon_status_str.restype = ctypes.c_char_p
+    lib.muon_last_error_detail.argtypes = []
+    lib.muon_last_error_detail.restype = ctypes.c_char_p
+    lib.muon_version.argtypes = []
+    lib.muon_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        detail = load_library().muon_last_error_detail().decode()
+        raise MuonError(status, detail)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return MUON_F32
+    if dt == torch.bfloat16:
+        return MUON_BF16
+    raise MuonError(3, f"unsupported dtype {dt}")
+
+
+def _as_shape(s: Sequence[int]) -> Tuple[int, int, int]:
+    s = tuple(int(x) for x in s)
+    if len(s) == 2:
+        return (1, s[0], s[1])
+    if len(s) == 3:
+        return s
+    raise MuonError(2, f"parameters must be 2-D or 3-D, got shape {s}")
+
+
+def _ptrs(tensors: Sequence[torch.Tensor]):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+class MuonPlan:
+    """Grouping plan for a fixed list of parameter shapes (muon_plan_create)."""
+
+    def __init__(self, shapes: Sequence[Sequence[int]], dtype: torch.dtype = torch.bfloat16):
+        lib = load_library()
+        self.shapes = [_as_shape(s) for s in shapes]
+        self.orig_shapes = [tuple(int(x) for x in s) for s in shapes]
+        self.dtype = dtype
+        n = len(self.shapes)
+        self._cshapes = (MuonShape * max(n, 1))(*[MuonShape(*s) for s in self.shapes])
+        h = ctypes.c_void_p()
+        code = _dtype_code(dtype)
+        _check(lib.muon_plan_create(self._cshapes, n, code, code, MUON_F32, ctypes.byref(h)))
+        self._h = h
+        b = ctypes.c_size_t()
+        _check(lib.muon_plan_workspace_bytes(self._h, ctypes.byref(b)))
+        self.workspace_bytes = int(b.value)
+
+    @classmethod
+    def for_params(cls, params: Sequence[torch.Tensor]) -> "MuonPlan":
+        dts = {p.dtype for p in params}
+        if len(dts) != 1:
+            raise MuonError(3, "all parameters of one plan share a dtype")
+        return cls([tuple(p.shape) for p in params], dts.pop())
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.muon_plan_destroy(h)
+            self._h = None
+
+    def groups(self) -> List[dict]:
+        lib = load_library()
+        n = ctypes.c_int32()
+        _check(lib.muon_plan_num_groups(self._h, ctypes.byref(n)))
+        out = []
+        for g in range(n.value):
+            v = [ctypes.c_int64() for _ in range(5)]
+            _check(lib.muon_plan_group_info(self._h, g, *[ctypes.byref(x) for x in v]))
+            out.append(dict(m=v[0].value, n=v[1].value, count=v[2].value,
+                            n_transposed=v[3].value, n_chunks=v[4].value))
+        return out
+
+    def new_workspace(self, device="cuda") -> torch.Tensor:
+        """Zero-filled workspace of the plan's size (a torch uint8 tensor)."""
+        return torch.zeros(self.workspace_bytes, dtype=torch.uint8, device=device)
+
+    def _check_tensors(self, ts: Sequence[torch.Tensor], dtype: torch.dtype, what: str):
+        if len(ts) != len(self.shapes):
+            raise MuonError(4, f"{what}: {len(ts)} tensors for a plan of {len(self.shapes)}")
+        for i, t in enumerate(ts):
+            if t.dtype != dtype:
+                raise MuonError(3, f"{what}[{i}] has dtype {t.dtype}, expected {dtype}")
+            if not t.is_contiguous():
+                raise MuonError(1, f"{what}[{i}] is not contiguous")
+            if not t.is_cuda:
+                raise MuonError(1, f"{what}[{i}] is not a device tensor")
+            if _as_shape(t.shape) != self.shapes[i]:
+                raise MuonError(4, f"{what}[{i}] has shape {tuple(t.shape)}")
+
+    @staticmethod
+    def _stream(stream) -> int:
+        s = stream if stream is not None else torch.cuda.current_stream()
+        return int(s.cuda_stream)
+
+    def step(self, params, grads, moms, *, lr: float, mu: float = 0.95, nesterov: bool = True,
+             wd: float = 0.0, coeffs=(3.4445, -4.7750, 2.0315), ns_steps: int = 5,
+             scale: float = 1.0, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+        """One Muon step (muon_step), enqueued on `stream` (default: current)."""
+        lib = load_library()
+        self._check_tensors(params, self.dtype, "params")
+        self._check_tensors(grads, self.dtype, "grads")
+        self._check_tensors(moms, torch.float32, "moms")
+        if workspace is None:
+            workspace = self._default_ws(params[0].device)
+        a, b, c = (float(x) for x in coeffs)
+        _check(lib.muon_step(self._h, _ptrs(params), _ptrs(grads), _ptrs(moms), self._cshapes,
+                             len(self.shapes), float(lr), float(mu), int(bool(nesterov)), float(wd),
+                             a, b, c, int(ns_steps), float(scale), ctypes.c_void_p(workspace.data_ptr()),
+                             workspace.numel(), ctypes.c_void_p(self._stream(stream))))
+
+    def ns(self, inputs, outputs, *, coeffs=(3.4445, -4.7750, 2.0315), ns_steps: int = 5,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+        """Newton-Schulz alone (muon_ns): outputs (fp32) = NS(inputs)."""
+        lib = load_library()
+        self._check_tensors(inputs, self.dtype, "inputs")
+        self._check_tensors(outputs, torch.float32, "outputs")
+        if workspace is None:
+            workspace = self._default_ws(inputs[0].device)
+        a, b, c = (float(x) for x in coeffs)
+        _check(lib.muon_ns(self._h, _ptrs(inputs), _ptrs(outputs), self._cshapes, len(self.shapes),
+                           a, b, c, int(ns_steps), ctypes.c_void_p(workspace.data_ptr()),
+                           workspace.numel(), ctypes.c_void_p(self._stream(stream))))
+
+    def _default_ws(self, device) -> torch.Tensor:
+        ws = getattr(self, "_ws", None)
+        if ws is None or ws.device != device:
+            ws = self.new_workspace(device)
+            self._ws = ws
+        return ws

@@ -1,0 +1,256 @@
+// C ABI entry points (include/muon.h): validation, per-chunk descriptor
+// tables, and the launch sequence on the caller's stream.  No device memory is
+// allocated or freed here and the host never waits for the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "launch.hpp"
+#include "plan.hpp"
+
+struct muon_plan_s {
+  muon::Plan p;
+};
+
+namespace {
+
+thread_local std::string g_detail;
+
+muon_status fail(muon_status s, const std::string& d) {
+  g_detail = d;
+  return s;
+}
+
+constexpr unsigned kSpinLimit = 1u << 20;  // bounded barrier wait (polls, about a second)
+
+// Co-resident workgroup capacity of the skinny kernel, per device id.
+std::mutex g_cap_mu;
+std::vector<int> g_cap;  // -1 = not queried
+
+muon_status skinny_capacity(int* cap) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_cap_mu);
+  if (int(g_cap.size()) <= dev) g_cap.resize(dev + 1, -1);
+  if (g_cap[dev] < 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return fail(MUON_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
+    g_cap[dev] = cus * muon::skinny_max_blocks_per_cu();
+  }
+  *cap = g_cap[dev];
+  return MUON_OK;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+
+muon_status check_shapes(const muon::Plan& P, const muon_shape* shapes, int32_t n_params) {
+  if (n_params != (int32_t)P.shapes.size())
+    return fail(MUON_ERR_PLAN_MISMATCH, "n_params " + std::to_string(n_params) + " != plan's " +
+                                            std::to_string(P.shapes.size()));
+  if (!shapes) return fail(MUON_ERR_INVALID_ARG, "shapes is null");
+  for (int32_t i = 0; i < n_params; ++i) {
+    const muon_shape& a = shapes[i];
+    const muon_shape& b = P.shapes[i];
+    if (a.batch != b.batch || a.rows != b.rows || a.cols != b.cols)
+      return fail(MUON_ERR_PLAN_MISMATCH, "shape of parameter " + std::to_string(i) + " differs from the plan");
+  }
+  return MUON_OK;
+}
+
+muon_status check_ptrs(const void* const* ptrs, int32_t n, const char* what) {
+  if (!ptrs) return fail(MUON_ERR_INVALID_ARG, std::string(what) + " array is null");
+  for (int32_t i = 0; i < n; ++i) {
+    if (!ptrs[i]) return fail(MUON_ERR_INVALID_ARG, std::string(what) + "[" + std::to_string(i) + "] is null");
+    if ((reinterpret_cast<uintptr_t>(ptrs[i]) & 15u) != 0)
+      return fail(MUON_ERR_ALIGNMENT, std::string(what) + "[" + std::to_string(i) + "] is not 16-byte aligned");
+  }
+  return MUON_OK;
+}
+
+size_t elem_size(muon_dtype d) { return d == MUON_BF16 ? 2 : 4; }
+
+// Enqueue every chunk of every group.  `w`, `g`, `m` are per-parameter device
+// pointers (m may be null for muon_ns).
+muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, void* const* m,
+                    const muon::StepScalars& sc, void* workspace, hipStream_t st) {
+  using namespace muon;
+  uint8_t* ws = (uint8_t*)workspace;
+  const size_t pes = elem_size(P.param_dt);
+  for (const Group& grp : P.groups) {
+    if (grp.path == PATH_SKINNY) {
+      int cap = 0;
+      muon_status s = skinny_capacity(&cap);
+      if (s != MUON_OK) return s;
+      if (int64_t(grp.max_chunk) * grp.slabs > cap)
+        return fail(MUON_ERR_HIP, "device holds only " + std::to_string(cap) +
+                                      " co-resident workgroups of the skinny kernel; a chunk needs " +
+                                      std::to_string(int64_t(grp.max_chunk) * grp.slabs));
+    }
+    for (const Chunk& ch : grp.chunks) {
+      MatTable tab;
+      std::memset(&tab, 0, sizeof(tab));
+      for (int32_t q = 0; q < ch.count; ++q) {
+        const MatEntry& me = P.mats[grp.mats[ch.first + q]];
+        const size_t off = size_t(me.e) * size_t(me.rows) * size_t(me.cols);
+        const size_t wes = (sc.mode == 1) ? 4 : pes;  // muon_ns writes fp32 O
+        tab.e[q].w = (uint8_t*)w[me.param] + off * wes;
+        tab.e[q].g = (const uint8_t*)g[me.param] + off * pes;
+        tab.e[q].m = m ? (float*)m[me.param] + off : nullptr;
+        tab.tr[q] = me.tr ? 1 : 0;
+      }
+      hipError_t e;
+      if (grp.path == PATH_SKINNY) {
+        SkinnyArgs a;
+        a.tab = tab;
+        a.sc = sc;
+        a.count = ch.count;
+        a.m = int(grp.m);
+        a.n = grp.n;
+        a.slabs = grp.slabs;
+        a.slab_w = grp.slab_w;
+        a.part = (float*)(ws + P.ws_dyn_off);
+        a.sync = (uint32_t*)(ws + P.ws_sync_off);
+        a.spin_limit = kSpinLimit;
+        e = run_skinny(a, st);
+      } else {
+        LargeArgs a;
+        a.tab = tab;
+        a.sc = sc;
+        a.L = large_layout(grp, ch.count, P.param_dt);
+        a.ws = ws + P.ws_dyn_off;
+        a.count = ch.count;
+        a.m = grp.m;
+        a.n = grp.n;
+        a.mp = grp.mp;
+        a.np = grp.np;
+        a.bf16 = (grp.path == PATH_MFMA);
+        e = run_large(a, st);
+      }
+      if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    }
+  }
+  return MUON_OK;
+}
+
+muon_status check_workspace(const muon::Plan& P, void* workspace, size_t bytes) {
+  if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is null");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MUON_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (bytes < P.ws_bytes)
+    return fail(MUON_ERR_WORKSPACE, "workspace has " + std::to_string(bytes) + " bytes, needs " +
+                                        std::to_string(P.ws_bytes));
+  return MUON_OK;
+}
+
+muon_status check_coeffs(float a, float b, float c, int32_t ns_steps) {
+  if (!finite(a) || !finite(b) || !finite(c)) return fail(MUON_ERR_INVALID_ARG, "NS coefficients must be finite");
+  if (ns_steps < 0 || ns_steps > 16) return fail(MUON_ERR_INVALID_ARG, "ns_steps must be in 0..16");
+  return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status muon_plan_create(const muon_shape* shapes, int32_t n_params, muon_dtype param_dt,
+                             muon_dtype grad_dt, muon_dtype mom_dt, muon_plan* out) {
+  if (!out) return fail(MUON_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  muon::Plan P;
+  std::string d;
+  muon_status s = muon::build_plan(shapes, n_params, param_dt, grad_dt, mom_dt, &P, &d);
+  if (s != MUON_OK) return fail(s, d);
+  muon_plan h = new (std::nothrow) muon_plan_s;
+  if (!h) return fail(MUON_ERR_INVALID_ARG, "out of host memory");
+  h->p = std::move(P);
+  *out = h;
+  return MUON_OK;
+}
+
+void muon_plan_destroy(muon_plan plan) { delete plan; }
+
+muon_status muon_plan_workspace_bytes(muon_plan plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(MUON_ERR_INVALID_ARG, "null argument");
+  *bytes = plan->p.ws_bytes;
+  return MUON_OK;
+}
+
+muon_status muon_plan_num_groups(muon_plan plan, int32_t* n_groups) {
+  if (!plan || !n_groups) return fail(MUON_ERR_INVALID_ARG, "null argument");
+  *n_groups = (int32_t)plan->p.groups.size();
+  return MUON_OK;
+}
+
+muon_status muon_plan_group_info(muon_plan plan, int32_t g, int64_t* m, int64_t* n, int64_t* count,
+                                 int64_t* n_transposed, int64_t* n_chunks) {
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "null plan");
+  if (g < 0 || g >= (int32_t)plan->p.groups.size()) return fail(MUON_ERR_INVALID_ARG, "group index out of range");
+  const muon::Group& G = plan->p.groups[g];
+  if (m) *m = G.m;
+  if (n) *n = G.n;
+  if (count) *count = (int64_t)G.mats.size();
+  if (n_transposed) *n_transposed = G.n_tr;
+  if (n_chunks) *n_chunks = (int64_t)G.chunks.size();
+  return MUON_OK;
+}
+
+muon_status muon_step(muon_plan plan, void* const* param_ptrs, const void* const* grad_ptrs,
+                      void* const* mom_ptrs, const muon_shape* shapes, int32_t n_params, float lr,
+                      float mu, int32_t nesterov, float wd, float a, float b, float c, int32_t ns_steps,
+                      float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "null plan");
+  const muon::Plan& P = plan->p;
+  muon_status s = check_shapes(P, shapes, n_params);
+  if (s != MUON_OK) return s;
+  if ((s = check_ptrs((const void* const*)param_ptrs, n_params, "param_ptrs")) != MUON_OK) return s;
+  if ((s = check_ptrs(grad_ptrs, n_params, "grad_ptrs")) != MUON_OK) return s;
+  if ((s = check_ptrs((const void* const*)mom_ptrs, n_params, "mom_ptrs")) != MUON_OK) return s;
+  if (!finite(lr) || !finite(mu) || !finite(wd) || !finite(scale))
+    return fail(MUON_ERR_INVALID_ARG, "lr, mu, wd and scale must be finite");
+  if (nesterov != 0 && nesterov != 1) return fail(MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1");
+  if ((s = check_coeffs(a, b, c, ns_steps)) != MUON_OK) return s;
+  if ((s = check_workspace(P, workspace, workspace_bytes)) != MUON_OK) return s;
+  muon::StepScalars sc{lr, mu, wd, scale, a, b, c, nesterov, ns_steps, 0};
+  return run_all(P, param_ptrs, grad_ptrs, mom_ptrs, sc, workspace, (hipStream_t)stream);
+}
+
+muon_status muon_ns(muon_plan plan, const void* const* in_ptrs, float* const* out_ptrs,
+                    const muon_shape* shapes, int32_t n_params, float a, float b, float c,
+                    int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "null plan");
+  const muon::Plan& P = plan->p;
+  muon_status s = check_shapes(P, shapes, n_params);
+  if (s != MUON_OK) return s;
+  if ((s = check_ptrs(in_ptrs, n_params, "in_ptrs")) != MUON_OK) return s;
+  if ((s = check_ptrs((const void* const*)out_ptrs, n_params, "out_ptrs")) != MUON_OK) return s;
+  if ((s = check_coeffs(a, b, c, ns_steps)) != MUON_OK) return s;
+  if ((s = check_workspace(P, workspace, workspace_bytes)) != MUON_OK) return s;
+  muon::StepScalars sc{0.f, 0.f, 0.f, 1.f, a, b, c, 0, ns_steps, 1};
+  return run_all(P, (void* const*)out_ptrs, in_ptrs, nullptr, sc, workspace, (hipStream_t)stream);
+}
+
+const char* muon_status_str(muon_status s) {
+  switch (s) {
+    case MUON_OK: return "MUON_OK";
+    case MUON_ERR_INVALID_ARG: return "MUON_ERR_INVALID_ARG";
+    case MUON_ERR_SHAPE: return "MUON_ERR_SHAPE";
+    case MUON_ERR_DTYPE: return "MUON_ERR_DTYPE";
+    case MUON_ERR_PLAN_MISMATCH: return "MUON_ERR_PLAN_MISMATCH";
+    case MUON_ERR_WORKSPACE: return "MUON_ERR_WORKSPACE";
+    case MUON_ERR_HIP: return "MUON_ERR_HIP";
+    case MUON_ERR_ALIGNMENT: return "MUON_ERR_ALIGNMENT";
+  }
+  return "MUON_ERR_UNKNOWN";
+}
+
+const char* muon_last_error_detail(void) { return g_detail.c_str(); }
+
+int32_t muon_version(void) { return 100; }
+
+}  // extern "C"

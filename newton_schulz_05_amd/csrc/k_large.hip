@@ -1,0 +1,548 @@
+// Kernels of the multi-launch path (bf16 MFMA for m > 32, and the fp32 path).
+//
+// Per chunk of matrices that share a wide shape (m <= n), with the workspace
+// buffers X [mp][np] (row-major NS iterate), Xt [np][mp] (its transpose, two
+// copies for ping-pong), A [mp][mp] fp32, and P:
+//   momentum_kernel   M <- mu*M + G; U = G + mu*M (or M); writes U into X and
+//                     Xt in the NS storage type and per-tile sums of U^2
+//   norm_kernel       s = 1 / (||U||_F + eps) per matrix, fixed-order sum
+//   gram (MFMA)       A = sc * X X^T on upper tiles, mirrored; also H = bf16(A)
+//                     and L = bf16(A - H) for the split A^2
+//   poly (MFMA)       S = H H + H L + L H  (A^2 to ~16 mantissa bits), then
+//                     P = ps * (a I + b A + c S); stores the off-diagonal part
+//                     in bf16 and the diagonal in fp32
+//   apply (MFMA)      X' = Poff Xt^T + diag(Pd) X; stores X' and X'^T in bf16,
+//                     or on the last step O (fp32) or the weight update
+// The fp32 path runs the same sequence with fp32 FMA tiles and a full fp32 P.
+//
+// The NS step itself (A = X X^T; X <- aX + (bA + cA^2)X) is Newton-Schulz on
+// the momentum as in item 1(1) of the HyperParallel FSDP Muon optimizer RFC;
+// batching matrices of one trailing shape in one launch is its item 3; the
+// decoupled decay in the last epilogue is its item 6.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace muon {
+
+// ============================================================================
+// momentum + Nesterov + per-tile sum of squares + NS input in both layouts
+// ============================================================================
+// One 64x64 tile of the matrix in its stored orientation [rows][cols] per
+// block; the grid covers the padded extent so that the padding of X and Xt is
+// written with zeros.
+template <typename PT, typename XT>
+__global__ __launch_bounds__(256) void momentum_kernel(MatTable tab, StepScalars sc, int tilesR,
+                                                       int tilesC, XT* __restrict__ X,
+                                                       XT* __restrict__ Xt0, int64_t xstride,
+                                                       int64_t mp, int64_t np, int64_t m,
+                                                       int64_t n, float* __restrict__ normpart,
+                                                       int64_t tiles) {
+  __shared__ float tileT[64][65];
+  __shared__ float red[4];
+  const int z = blockIdx.y;
+  const bool tr = tab.tr[z] != 0;
+  const int64_t rows = tr ? n : m, cols = tr ? m : n;        // stored shape
+  const int64_t rowsP = tr ? np : mp, colsP = tr ? mp : np;  // padded stored shape
+  const int tile = blockIdx.x;
+  const int tC = tr ? tilesR : tilesC;                       // tiles per stored row
+  const int64_t r0 = int64_t(tile / tC) * 64, c0 = int64_t(tile % tC) * 64;
+  const int t = threadIdx.x;
+  const int cg = t & 15, rg = t >> 4;
+  const PT* G = (const PT*)tab.e[z].g;
+  float* M = tab.e[z].m;
+  XT* nat = (tr ? Xt0 : X) + int64_t(z) * xstride;  // same orientation as the stored matrix
+  XT* trn = (tr ? X : Xt0) + int64_t(z) * xstride;  // transposed
+  const int64_t ldn = colsP, ldt = rowsP;
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int lr = rg + 16 * q;
+    const int64_t r = r0 + lr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int lc = cg * 4 + j;
+      const int64_t c = c0 + lc;
+      float u = 0.f;
+      if (r < rows && c < cols) {
+        const int64_t idx = r * cols + c;
+        const float g = Elem<PT>::load(G + idx);
+        if (sc.mode == 0) {
+          const float mn = fmaf(sc.mu, M[idx], g);
+          M[idx] = mn;
+          u = sc.nesterov ? fmaf(sc.mu, mn, g) : mn;
+        } else {
+          u = g;
+        }
+        ss = fmaf(u, u, ss);
+      }
+      // the value stored is what NS consumes (rounded to the storage type)
+      XT xv;
+      Elem<XT>::store(&xv, u);
+      const float ur = Elem<XT>::load(&xv);
+      if (r < rowsP && c < colsP) nat[r * ldn + c] = xv;
+      tileT[lr][lc] = ur;
+    }
+  }
+  __syncthreads();
+  // transposed copy: row (c0 + lc) of trn, columns r0 .. r0+63
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int lc = rg + 16 * q;
+    const int64_t c = c0 + lc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int lr = cg * 4 + j;
+      const int64_t r = r0 + lr;
+      if (c < colsP && r < rowsP) {
+        XT xv;
+        Elem<XT>::store(&xv, tileT[lr][lc]);
+        trn[c * ldt + r] = xv;
+      }
+    }
+  }
+  const float tot = block_sum_256(ss, red);
+  if (t == 0) normpart[int64_t(z) * tiles + tile] = tot;
+}
+
+// s = 1 / (sqrt(sum of squares) + eps); scal[z] = {s, s^2, sumsq, 0}
+__global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ normpart, int64_t tiles,
+                                                   float* __restrict__ scal) {
+  __shared__ float red[4];
+  const int z = blockIdx.x;
+  const float* p = normpart + int64_t(z) * tiles;
+  float v = 0.f;
+  for (int64_t i = threadIdx.x; i < tiles; i += 256) v += p[i];
+  const float tot = block_sum_256(v, red);
+  if (threadIdx.x == 0) {
+    const float s = 1.0f / (sqrtf(tot) + kNsEps);
+    scal[z * 4 + 0] = s;
+    scal[z * 4 + 1] = s * s;
+    scal[z * 4 + 2] = tot;
+    scal[z * 4 + 3] = 0.f;
+  }
+}
+
+// ============================================================================
+// Epilogues.  The GEMM mainloops hand each a run of 4 consecutive rows
+// (i0 .. i0+3) of one column j; `diag` is true on tiles on the diagonal of a
+// symmetric output, where only i <= j is owned (and mirrored to (j, i)).
+// ============================================================================
+struct NatStore {
+  // store O (fp32) or apply the weight update at the matrix's stored position
+  template <typename PT>
+  __device__ static __forceinline__ void put(const MatRef& r, const StepScalars& sc, bool tr,
+                                             int64_t m, int64_t n, int64_t i, int64_t j, float o) {
+    if (i >= m || j >= n) return;
+    const int64_t idx = tr ? (j * m + i) : (i * n + j);
+    if (sc.mode == 1) {
+      ((float*)r.w)[idx] = o;
+    } else {
+      PT* W = (PT*)r.w;
+      const float w = Elem<PT>::load(W + idx);
+      const float keep = 1.0f - sc.lr * sc.wd;
+      Elem<PT>::store(W + idx, fmaf(-sc.lr * sc.scale, o, w * keep));
+    }
+  }
+};
+
+// Gram (bf16 path): A = sc2 * acc, plus its bf16 hi/lo split
+struct EpiGramBf16 {
+  float* A; uint16_t* H; uint16_t* L; const float* scal; int use_scale; int64_t mp;
+  __device__ __forceinline__ void operator()(int z, int64_t i0, int64_t j, const float* v, bool diag) const {
+    const float s2 = use_scale ? scal[z * 4 + 1] : 1.0f;
+    const int64_t base = int64_t(z) * mp * mp;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = i0 + q;
+      if (diag && i > j) continue;
+      const float a = v[q] * s2;
+      const uint16_t h = f2bf(a);
+      const uint16_t l = f2bf(a - bf2f(h));
+      A[base + i * mp + j] = a; H[base + i * mp + j] = h; L[base + i * mp + j] = l;
+      if (i != j) { A[base + j * mp + i] = a; H[base + j * mp + i] = h; L[base + j * mp + i] = l; }
+    }
+  }
+};
+
+// Poly (bf16 path): P = ps*(a I + b A + c S); off-diagonal bf16, diagonal fp32
+struct EpiPolyBf16 {
+  const float* A; uint16_t* Poff; float* Pd; const float* scal; int use_scale;
+  float a, b, c; int64_t mp, m;
+  __device__ __forceinline__ void operator()(int z, int64_t i0, int64_t j, const float* v, bool diag) const {
+    const float ps = use_scale ? scal[z * 4 + 0] : 1.0f;
+    const int64_t base = int64_t(z) * mp * mp;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = i0 + q;
+      if (diag && i > j) continue;
+      const float av = A[base + i * mp + j];
+      float p = fmaf(c, v[q], b * av);
+      if (i == j) {
+        p = ps * (p + a);
+        Poff[base + i * mp + j] = 0;
+        Pd[int64_t(z) * mp + i] = (i < m) ? p : 0.f;
+      } else {
+        p = ps * p;
+        const uint16_t ph = f2bf(p);
+        Poff[base + i * mp + j] = ph;
+        Poff[base + j * mp + i] = ph;
+      }
+    }
+  }
+};
+
+// Apply (bf16 path): X' = acc + Pd[i] * X[i][j]
+template <typename PT>
+struct EpiApplyBf16 {
+  MatTable tab; StepScalars sc; uint16_t* X; uint16_t* XtN; const float* Pd;
+  int64_t mp, np, m, n; int last;
+  __device__ __forceinline__ void operator()(int z, int64_t i0, int64_t j, const float* v, bool) const {
+    uint16_t* Xz = X + int64_t(z) * mp * np;
+    float o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = i0 + q;
+      o[q] = fmaf(Pd[int64_t(z) * mp + i], bf2f(Xz[i * np + j]), v[q]);
+    }
+    if (!last) {
+      u16x4 pk;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        pk[q] = f2bf(o[q]);
+        Xz[(i0 + q) * np + j] = pk[q];
+      }
+      *(u16x4*)(XtN + int64_t(z) * mp * np + j * mp + i0) = pk;
+    } else {
+      const bool tr = tab.tr[z] != 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) NatStore::put<PT>(tab.e[z], sc, tr, m, n, i0 + q, j, o[q]);
+    }
+  }
+};
+
+// fp32 path epilogues
+struct EpiGramF32 {
+  float* A; const float* scal; int use_scale; int64_t mp;
+  __device__ __forceinline__ void operator()(int z, int64_t i0, int64_t j, const float* v, bool diag) const {
+    const float s2 = use_scale ? scal[z * 4 + 1] : 1.0f;
+    const int64_t base = int64_t(z) * mp * mp;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = i0 + q;
+      if (diag && i > j) continue;
+      const float a = v[q] * s2;
+      A[base + i * mp + j] = a;
+      if (i != j) A[base + j * mp + i] = a;
+    }
+  }
+};
+
+struct EpiPolyF32 {
+  const float* A; float* P; const float* scal; int use_scale; float a, b, c; int64_t mp, m;
+  __device__ __forceinline__ void operator()(int z, int64_t i0, int64_t j, const float* v, bool diag) const {
+    const float ps = use_scale ? scal[z * 4 + 0] : 1.0f;
+    const int64_t base = int64_t(z) * mp * mp;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = i0 + q;
+      if (diag && i > j) continue;
+      float p = fmaf(c, v[q], b * A[base + i * mp + j]);
+      if (i == j) p = (i < m) ? ps * (p + a) : 0.f; else p = ps * p;
+      P[base + i * mp + j] = p;
+      if (i != j) P[base + j * mp + i] = p;
+    }
+  }
+};
+
+template <typename PT>
+struct EpiApplyF32 {
+  MatTable tab; StepScalars sc; float* X; float* XtN;
+  int64_t mp, np, m, n; int last;
+  __device__ __forceinline__ void operator()(int z, int64_t i0, int64_t j, const float* v, bool) const {
+    if (!last) {
+      float* Xz = X + int64_t(z) * mp * np;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Xz[(i0 + q) * np + j] = v[q];
+      *(f32x4*)(XtN + int64_t(z) * mp * np + j * mp + i0) = f32x4{v[0], v[1], v[2], v[3]};
+    } else {
+      const bool tr = tab.tr[z] != 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) NatStore::put<PT>(tab.e[z], sc, tr, m, n, i0 + q, j, v[q]);
+    }
+  }
+};
+
+// ============================================================================
+// Tile scheduling: full grid or upper triangle (symmetric outputs)
+// ============================================================================
+__device__ __forceinline__ void tile_coords(int t, int T, bool upper, int& ti, int& tj) {
+  if (!upper) { ti = t / T; tj = t % T; return; }
+  int r = 0, len = T;
+  while (t >= len) { t -= len; ++r; --len; }
+  ti = r; tj = r + t;
+}
+
+// ============================================================================
+// bf16 MFMA GEMM, "NT": C[i][j] = sum_k A[i][k] * B[j][k] (+ split products)
+// A, B row-major with k contiguous; all dims padded to the tile sizes.
+// 128x128 output tile per block of 256 threads (2x2 waves of 64x64), BK = 64,
+// LDS double buffered, 16-byte chunks XOR-swizzled by row.
+// NPROD = 1: C = A B^T.   NPROD = 3: C = Ah Bh^T + Ah Bl^T + Al Bh^T.
+// ============================================================================
+constexpr int GB_M = 128, GB_N = 128, GB_K = 64;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
+template <int NPROD, typename Epi>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al, int64_t lda, int64_t sA,
+    const uint16_t* __restrict__ Bh, const uint16_t* __restrict__ Bl, int64_t ldb, int64_t sB,
+    int64_t K, int tilesN, int upper, Epi epi) {
+  constexpr int NA = (NPROD == 3) ? 2 : 1;   // operand planes per side
+  __shared__ u16x8 lds[2][NA * 2][GB_M * GB_K / 8];  // [stage][plane: Ah, (Al), Bh, (Bl)]
+  const int z = blockIdx.y;
+  int ti, tj;
+  tile_coords(blockIdx.x, tilesN, upper != 0, ti, tj);
+  const int64_t row0 = int64_t(ti) * GB_M, col0 = int64_t(tj) * GB_N;
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int wr = (wid >> 1) * 64, wc = (wid & 1) * 64;
+
+  const uint16_t* gA[NA];
+  const uint16_t* gB[NA];
+  gA[0] = Ah + int64_t(z) * sA + row0 * lda;
+  gB[0] = Bh + int64_t(z) * sB + col0 * ldb;
+  if (NA == 2) {
+    gA[NA - 1] = Al + int64_t(z) * sA + row0 * lda;
+    gB[NA - 1] = Bl + int64_t(z) * sB + col0 * ldb;
+  }
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  u16x8 ra[NA][4], rb[NA][4];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int q = t + 256 * p, r = q >> 3, ch = q & 7;
+#pragma unroll
+      for (int s = 0; s < NA; ++s) {
+        ra[s][p] = *(const u16x8*)(gA[s] + int64_t(r) * lda + k0 + ch * 8);
+        rb[s][p] = *(const u16x8*)(gB[s] + int64_t(r) * ldb + k0 + ch * 8);
+      }
+    }
+  };
+  auto sstore = [&](int st) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int q = t + 256 * p, r = q >> 3, ch = q & 7;
+#pragma unroll
+      for (int s = 0; s < NA; ++s) {
+        lds[st][s][swz(r, ch)] = ra[s][p];
+        lds[st][NA + s][swz(r, ch)] = rb[s][p];
+      }
+    }
+  };
+
+  const int KT = int(K / GB_K);
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < KT) gload(int64_t(kt + 1) * GB_K);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = ks * 2 + (lane >> 5);
+      bf16x8 fa[NA][2], fb[NA][2];
+#pragma unroll
+      for (int s = 0; s < NA; ++s)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          fa[s][x] = as_bf16x8(lds[st][s][swz(wr + x * 32 + (lane & 31), ch)]);
+          fb[s][x] = as_bf16x8(lds[st][NA + s][swz(wc + x * 32 + (lane & 31), ch)]);
+        }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          acc[a][b] = mfma32x32x16(fa[0][a], fb[0][b], acc[a][b]);
+          if (NPROD == 3) {
+            acc[a][b] = mfma32x32x16(fa[0][a], fb[NA - 1][b], acc[a][b]);
+            acc[a][b] = mfma32x32x16(fa[NA - 1][a], fb[0][b], acc[a][b]);
+          }
+        }
+    }
+    if (kt + 1 < KT) sstore(st ^ 1);
+    __syncthreads();
+  }
+
+  const bool diag = upper && (ti == tj);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t i0 = row0 + wr + a * 32 + g * 8 + (lane >> 5) * 4;
+        const int64_t j = col0 + wc + b * 32 + (lane & 31);
+        float v[4] = {acc[a][b][g * 4 + 0], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2],
+                      acc[a][b][g * 4 + 3]};
+        epi(z, i0, j, v, diag);
+      }
+}
+
+// ============================================================================
+// fp32 FMA GEMM, NT, 64x64 tile, BK = 16, 256 threads with 4x4 outputs each
+// ============================================================================
+constexpr int GF_M = 64, GF_K = 16;
+
+template <typename Epi>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int64_t lda,
+                                                       int64_t sA, const float* __restrict__ B,
+                                                       int64_t ldb, int64_t sB, int64_t K,
+                                                       int tilesN, int upper, Epi epi) {
+  __shared__ float As[GF_K][GF_M + 4];
+  __shared__ float Bs[GF_K][GF_M + 4];
+  const int z = blockIdx.y;
+  int ti, tj;
+  tile_coords(blockIdx.x, tilesN, upper != 0, ti, tj);
+  const int64_t row0 = int64_t(ti) * GF_M, col0 = int64_t(tj) * GF_M;
+  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  const float* gA = A + int64_t(z) * sA + row0 * lda;
+  const float* gB = B + int64_t(z) * sB + col0 * ldb;
+  float acc[4][4] = {};
+  const int lr = t >> 2, lk = (t & 3) * 4;
+  for (int64_t k0 = 0; k0 < K; k0 += GF_K) {
+    const f32x4 va = *(const f32x4*)(gA + int64_t(lr) * lda + k0 + lk);
+    const f32x4 vb = *(const f32x4*)(gB + int64_t(lr) * ldb + k0 + lk);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { As[lk + q][lr] = va[q]; Bs[lk + q][lr] = vb[q]; }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < GF_K; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { a[q] = As[k][ty * 4 + q]; b[q] = Bs[k][tx * 4 + q]; }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+    }
+  }
+  const bool diag = upper && (ti == tj);
+#pragma unroll
+  for (int y = 0; y < 4; ++y) {
+    float v[4] = {acc[0][y], acc[1][y], acc[2][y], acc[3][y]};
+    epi(z, row0 + ty * 4, col0 + tx * 4 + y, v, diag);
+  }
+}
+
+// ============================================================================
+// ns_steps == 0: O = s * U taken from X, then the store / update
+// ============================================================================
+template <typename PT, typename XT>
+__global__ __launch_bounds__(256) void ns0_kernel(MatTable tab, StepScalars sc, const XT* __restrict__ X,
+                                                  int64_t mp, int64_t np, int64_t m, int64_t n,
+                                                  const float* __restrict__ scal) {
+  const int z = blockIdx.y;
+  const bool tr = tab.tr[z] != 0;
+  const float s = scal[z * 4 + 0];
+  const XT* Xz = X + int64_t(z) * mp * np;
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < m * n; e += int64_t(gridDim.x) * 256) {
+    const int64_t i = e / n, j = e % n;
+    NatStore::put<PT>(tab.e[z], sc, tr, m, n, i, j, s * Elem<XT>::load(Xz + i * np + j));
+  }
+}
+
+// ============================================================================
+// Host launchers
+// ============================================================================
+static hipError_t last_launch() { return hipGetLastError(); }
+
+template <typename PT, typename XT>
+static hipError_t run_large_t(const LargeArgs& g, hipStream_t st) {
+  const LargeLayout& L = g.L;
+  uint8_t* ws = (uint8_t*)g.ws;
+  XT* X = (XT*)(ws + L.x);
+  XT* Xt[2] = {(XT*)(ws + L.xt0), (XT*)(ws + L.xt1)};
+  float* A = (float*)(ws + L.a);
+  float* normpart = (float*)(ws + L.normpart);
+  float* scal = (float*)(ws + L.scal);
+  const int64_t mp = g.mp, np = g.np, m = g.m, n = g.n;
+  const int count = g.count;
+
+  // momentum: 64x64 tiles over the padded matrix (64 divides mp and np)
+  {
+    const int tilesM = int(mp / 64), tilesN = int(np / 64);
+    dim3 grid(unsigned(tilesM * tilesN), unsigned(count));
+    hipLaunchKernelGGL((momentum_kernel<PT, XT>), grid, dim3(256), 0, st, g.tab, g.sc, tilesM,
+                       tilesN, X, Xt[0], L.x_stride, mp, np, m, n, normpart, L.tiles);
+    if (hipError_t e = last_launch(); e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(norm_kernel, dim3(count), dim3(256), 0, st, normpart, L.tiles, scal);
+  if (hipError_t e = last_launch(); e != hipSuccess) return e;
+
+  const int steps = g.sc.ns_steps;
+  if (steps == 0) {
+    hipLaunchKernelGGL((ns0_kernel<PT, XT>), dim3(unsigned(std::min<int64_t>(4096, (m * n + 255) / 256)), count),
+                       dim3(256), 0, st, g.tab, g.sc, X, mp, np, m, n, scal);
+    return last_launch();
+  }
+  int cur = 0;
+  for (int k = 0; k < steps; ++k) {
+    const int last = (k == steps - 1);
+    if constexpr (sizeof(XT) == 2) {
+      uint16_t* H = (uint16_t*)(ws + L.h);
+      uint16_t* Lo = (uint16_t*)(ws + L.l);
+      uint16_t* Poff = (uint16_t*)(ws + L.poff);
+      float* Pd = (float*)(ws + L.pdiag);
+      const int Tm = int(mp / GB_M), Tn = int(np / GB_N);
+      // Gram: upper tiles of [mp x mp], K = np
+      EpiGramBf16 eg{A, H, Lo, scal, k == 0, mp};
+      hipLaunchKernelGGL((gemm_bf16_kernel<1, EpiGramBf16>), dim3(unsigned(Tm * (Tm + 1) / 2), count),
+                         dim3(256), 0, st, (const uint16_t*)X, (const uint16_t*)nullptr, np, L.x_stride,
+                         (const uint16_t*)X, (const uint16_t*)nullptr, np, L.x_stride, np, Tm, 1, eg);
+      if (hipError_t e = last_launch(); e != hipSuccess) return e;
+      // Poly: S = HH + HL + LH over upper tiles, K = mp
+      EpiPolyBf16 ep{A, Poff, Pd, scal, k == 0, g.sc.a, g.sc.b, g.sc.c, mp, m};
+      hipLaunchKernelGGL((gemm_bf16_kernel<3, EpiPolyBf16>), dim3(unsigned(Tm * (Tm + 1) / 2), count),
+                         dim3(256), 0, st, (const uint16_t*)H, (const uint16_t*)Lo, mp, L.a_stride,
+                         (const uint16_t*)H, (const uint16_t*)Lo, mp, L.a_stride, mp, Tm, 1, ep);
+      if (hipError_t e = last_launch(); e != hipSuccess) return e;
+      // Apply: X' = Poff Xt^T + diag(Pd) X, K = mp
+      EpiApplyBf16<PT> ea{g.tab, g.sc, (uint16_t*)X, (uint16_t*)Xt[cur ^ 1], Pd, mp, np, m, n, last};
+      hipLaunchKernelGGL((gemm_bf16_kernel<1, EpiApplyBf16<PT>>), dim3(unsigned(Tm * Tn), count),
+                         dim3(256), 0, st, (const uint16_t*)Poff, (const uint16_t*)nullptr, mp, L.a_stride,
+                         (const uint16_t*)Xt[cur], (const uint16_t*)nullptr, mp, L.x_stride, mp, Tn, 0, ea);
+      if (hipError_t e = last_launch(); e != hipSuccess) return e;
+    } else {
+      float* Pf = (float*)(ws + L.poff);
+      const int Tm = int(mp / GF_M), Tn = int(np / GF_M);
+      EpiGramF32 eg{A, scal, k == 0, mp};
+      hipLaunchKernelGGL((gemm_f32_kernel<EpiGramF32>), dim3(unsigned(Tm * (Tm + 1) / 2), count), dim3(256),
+                         0, st, (const float*)X, np, L.x_stride, (const float*)X, np, L.x_stride, np, Tm, 1, eg);
+      if (hipError_t e = last_launch(); e != hipSuccess) return e;
+      EpiPolyF32 ep{A, Pf, scal, k == 0, g.sc.a, g.sc.b, g.sc.c, mp, m};
+      hipLaunchKernelGGL((gemm_f32_kernel<EpiPolyF32>), dim3(unsigned(Tm * (Tm + 1) / 2), count), dim3(256),
+                         0, st, (const float*)A, mp, L.a_stride, (const float*)A, mp, L.a_stride, mp, Tm, 1, ep);
+      if (hipError_t e = last_launch(); e != hipSuccess) return e;
+      EpiApplyF32<PT> ea{g.tab, g.sc, (float*)X, (float*)Xt[cur ^ 1], mp, np, m, n, last};
+      hipLaunchKernelGGL((gemm_f32_kernel<EpiApplyF32<PT>>), dim3(unsigned(Tm * Tn), count), dim3(256), 0,
+                         st, (const float*)Pf, mp, L.a_stride, (const float*)Xt[cur], mp, L.x_stride, mp, Tn, 0, ea);
+      if (hipError_t e = last_launch(); e != hipSuccess) return e;
+    }
+    cur ^= 1;
+  }
+  return hipSuccess;
+}
+
+hipError_t run_large(const LargeArgs& g, hipStream_t st) {
+  if (g.bf16) return run_large_t<uint16_t, uint16_t>(g, st);
+  return run_large_t<float, float>(g, st);
+}
+
+}  // namespace muon

@@ -1,0 +1,154 @@
+// Host-side plan construction (see plan.hpp).
+#include "plan.hpp"
+
+#include <algorithm>
+#include <map>
+#include <utility>
+
+namespace muon {
+
+namespace {
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Split `count` matrices into the fewest chunks of at most `cap` each, with
+// sizes as even as possible (the split never changes any result: every matrix
+// is computed the same way in any chunk).
+std::vector<Chunk> split_even(int32_t count, int32_t cap) {
+  std::vector<Chunk> out;
+  if (cap < 1) cap = 1;
+  int32_t n = (count + cap - 1) / cap;
+  int32_t base = count / n, extra = count % n, first = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t c = base + (i < extra ? 1 : 0);
+    out.push_back(Chunk{first, c});
+    first += c;
+  }
+  return out;
+}
+
+}  // namespace
+
+LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
+  LargeLayout L{};
+  const size_t es = (param_dt == MUON_BF16) ? 2 : 4;  // X element size
+  const int64_t mp = g.mp, np = g.np;
+  L.x_stride = mp * np;
+  L.a_stride = mp * mp;
+  // the momentum kernel's 64x64 tiles cover the padded matrix
+  L.tiles = (mp / kMomTile) * (np / kMomTile);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t xb = size_t(count) * size_t(mp) * size_t(np) * es;
+  L.x = take(xb);
+  L.xt0 = take(xb);
+  L.xt1 = take(xb);
+  L.a = take(size_t(count) * size_t(mp) * size_t(mp) * 4);
+  if (param_dt == MUON_BF16) {
+    L.h = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+    L.l = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+    L.poff = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+  } else {
+    L.h = L.l = 0;
+    L.poff = take(size_t(count) * size_t(mp) * size_t(mp) * 4);  // full fp32 P
+  }
+  L.pdiag = take(size_t(count) * size_t(mp) * 4);
+  L.normpart = take(size_t(count) * size_t(L.tiles) * 4);
+  L.scal = take(size_t(count) * 4 * 4);
+  L.bytes = off;
+  return L;
+}
+
+size_t skinny_bytes(const Group& g, int32_t count) {
+  return size_t(count) * 2 * size_t(g.slabs) * size_t(kSkinnyPartStride) * 4;
+}
+
+muon_status build_plan(const muon_shape* shapes, int32_t n_params, muon_dtype param_dt,
+                       muon_dtype grad_dt, muon_dtype mom_dt, Plan* out, std::string* detail) {
+  if (!shapes || !out) { *detail = "null shapes or output pointer"; return MUON_ERR_INVALID_ARG; }
+  if (n_params < 1) { *detail = "n_params must be >= 1"; return MUON_ERR_INVALID_ARG; }
+  if (param_dt != MUON_F32 && param_dt != MUON_BF16) {
+    *detail = "param dtype must be MUON_F32 or MUON_BF16"; return MUON_ERR_DTYPE;
+  }
+  if (grad_dt != param_dt) { *detail = "grad dtype must equal param dtype"; return MUON_ERR_DTYPE; }
+  if (mom_dt != MUON_F32) { *detail = "momentum dtype must be MUON_F32"; return MUON_ERR_DTYPE; }
+
+  Plan P;
+  P.param_dt = param_dt;
+  P.grad_dt = grad_dt;
+  P.mom_dt = mom_dt;
+  P.shapes.assign(shapes, shapes + n_params);
+
+  // key (m, n) -> group index, groups in order of first appearance
+  std::map<std::pair<int64_t, int64_t>, int32_t> key2g;
+  for (int32_t i = 0; i < n_params; ++i) {
+    const muon_shape& s = shapes[i];
+    if (s.batch < 1 || s.rows < 1 || s.cols < 1) {
+      *detail = "parameter " + std::to_string(i) + ": every dimension must be >= 1 "
+                "(1-D parameters belong to another optimizer)";
+      return MUON_ERR_SHAPE;
+    }
+    if (s.rows > (int64_t(1) << 31) || s.cols > (int64_t(1) << 31) ||
+        s.rows * s.cols > (int64_t(1) << 40)) {
+      *detail = "parameter " + std::to_string(i) + ": matrix too large";
+      return MUON_ERR_SHAPE;
+    }
+    const int64_t m = std::min(s.rows, s.cols), n = std::max(s.rows, s.cols);
+    auto key = std::make_pair(m, n);
+    auto it = key2g.find(key);
+    int32_t gi;
+    if (it == key2g.end()) {
+      gi = (int32_t)P.groups.size();
+      key2g[key] = gi;
+      Group g;
+      g.m = m;
+      g.n = n;
+      P.groups.push_back(g);
+    } else {
+      gi = it->second;
+    }
+    for (int64_t e = 0; e < s.batch; ++e) {
+      MatEntry me{i, e, s.rows, s.cols, s.rows > s.cols};
+      P.groups[gi].mats.push_back((int32_t)P.mats.size());
+      if (me.tr) P.groups[gi].n_tr++;
+      P.mats.push_back(me);
+    }
+  }
+
+  size_t dyn = 0;
+  for (Group& g : P.groups) {
+    const int32_t count = (int32_t)g.mats.size();
+    if (param_dt == MUON_F32) {
+      g.path = PATH_F32;
+    } else if (g.m <= kSkinnyMaxM && ceil_div(g.n, kSkinnyMaxSlab) <= kSkinnyCapacity) {
+      g.path = PATH_SKINNY;
+    } else {
+      g.path = PATH_MFMA;
+    }
+    if (g.path == PATH_SKINNY) {
+      g.slabs = (int32_t)ceil_div(g.n, kSkinnyMaxSlab);
+      g.slab_w = round_up(ceil_div(g.n, g.slabs), 32);
+      int32_t cap = (int32_t)std::min<int64_t>(kMaxChunkMats, kSkinnyCapacity / g.slabs);
+      g.chunks = split_even(count, cap);
+    } else {
+      const int64_t t = (g.path == PATH_MFMA) ? kMfmaTile : kF32Tile;
+      g.mp = round_up(g.m, t);
+      g.np = round_up(g.n, t);
+      LargeLayout one = large_layout(g, 1, param_dt);
+      int32_t cap = (int32_t)std::max<size_t>(1, kChunkBytesCap / std::max<size_t>(one.bytes, 1));
+      cap = std::min(cap, kMaxChunkMats);
+      g.chunks = split_even(count, cap);
+    }
+    for (const Chunk& c : g.chunks) g.max_chunk = std::max(g.max_chunk, c.count);
+    size_t need = (g.path == PATH_SKINNY) ? skinny_bytes(g, g.max_chunk)
+                                          : large_layout(g, g.max_chunk, param_dt).bytes;
+    dyn = std::max(dyn, need);
+  }
+  P.ws_sync_off = 0;
+  P.ws_dyn_off = kSyncBytes;
+  P.ws_bytes = kSyncBytes + align256(dyn);
+  *out = std::move(P);
+  return MUON_OK;
+}
+
+}  // namespace muon

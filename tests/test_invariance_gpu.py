@@ -1,0 +1,117 @@
+"""Bitwise invariances of the HIP path: results depend on nothing but the
+matrix itself.  Batching (RFC item 3) and expert slicing (RFC item 2) must
+not change a single bit of any matrix's momentum, weight or O."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from newton_schulz_05_amd import MuonPlan
+from newton_schulz_05_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _step(shapes, params, grads, dtype, steps=2):
+    plan = MuonPlan(shapes, dtype)
+    moms = [torch.zeros(p.shape, dtype=torch.float32, device=DEV) for p in params]
+    for s in range(steps):
+        plan.step(params, grads[s], moms, lr=0.02, wd=0.1)
+    torch.cuda.synchronize()
+    return params, moms
+
+
+def _draw(shapes, dtype, seed):
+    wl = WL.custom(shapes, dtype=dtype, number=seed)
+    return WL.make_params(wl, DEV, "cpu"), [WL.make_grads(wl, s, DEV, "cpu") for s in range(2)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shapes", [
+    [(24, 3000)] * 5,
+    [(100, 300)] * 3 + [(300, 100)] * 2,
+    [(130, 260)] * 4,
+], ids=["skinny", "mfma_mixed_orientation", "mfma_ragged"])
+def test_grouped_equals_alone(shapes, dtype):
+    params, grads = _draw(shapes, dtype, 71)
+    pa = [p.clone() for p in params]
+    pg, mg = _step(shapes, pa, grads, dtype)
+    for i, s in enumerate(shapes):
+        p1 = [params[i].clone()]
+        g1 = [[grads[0][i]], [grads[1][i]]]
+        p1, m1 = _step([s], p1, g1, dtype)
+        assert torch.equal(p1[0], pg[i]), f"W[{i}] differs when computed alone"
+        assert torch.equal(m1[0], mg[i]), f"M[{i}] differs when computed alone"
+
+
+def test_batch_position_and_order():
+    shapes = [(48, 512)] * 4
+    params, grads = _draw(shapes, torch.bfloat16, 72)
+    pa, _ = _step(shapes, [p.clone() for p in params], grads, torch.bfloat16)
+    perm = [2, 0, 3, 1]
+    pb, _ = _step(shapes, [params[i].clone() for i in perm],
+                  [[g[i] for i in perm] for g in grads], torch.bfloat16)
+    for k, i in enumerate(perm):
+        assert torch.equal(pb[k], pa[i])
+
+
+def test_expert_slices_independent():
+    """Perturbing expert j's gradient leaves every other expert bit-identical."""
+    for shape in [(6, 48, 40), (4, 24, 1000)]:
+        params, grads = _draw([shape], torch.bfloat16, 73)
+        pa, ma = _step([shape], [params[0].clone()], grads, torch.bfloat16)
+        g2 = [[g[0].clone()] for g in grads]
+        g2[0][0][2].mul_(30.0)
+        g2[1][0][2, 0, 0] = 5.0
+        pb, mb = _step([shape], [params[0].clone()], g2, torch.bfloat16)
+        others = [e for e in range(shape[0]) if e != 2]
+        assert torch.equal(pa[0][others], pb[0][others])
+        assert torch.equal(ma[0][others], mb[0][others])
+        assert not torch.equal(pa[0][2], pb[0][2])
+
+
+def test_slab_equals_separate_matrices():
+    shape = (5, 64, 96)
+    params, grads = _draw([shape], torch.bfloat16, 74)
+    pa, ma = _step([shape], [params[0].clone()], grads, torch.bfloat16)
+    sep = [tuple(shape[1:])] * shape[0]
+    pb, mb = _step(sep, [params[0][e].clone() for e in range(shape[0])],
+                   [[g[0][e] for e in range(shape[0])] for g in grads], torch.bfloat16)
+    for e in range(shape[0]):
+        assert torch.equal(pa[0][e], pb[e]) and torch.equal(ma[0][e], mb[e])
+
+
+def test_run_to_run_deterministic():
+    wl = WL.WORKLOADS["c3"]
+    outs = []
+    for _ in range(2):
+        params = WL.make_params(wl, DEV, "cpu")
+        moms = WL.make_moms(wl, DEV)
+        plan = MuonPlan(wl.shapes, wl.dtype)
+        for s in range(2):
+            plan.step(params, WL.make_grads(wl, s, DEV, "cpu"), moms, **wl.hyper())
+        torch.cuda.synchronize()
+        outs.append([p.clone() for p in params] + [m.clone() for m in moms])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_checkpoint_resume_bitwise():
+    """k steps, save W and M, one more step == the uninterrupted run."""
+    wl = WL.custom([(24, 2000), (96, 160)], number=75)
+    plan = MuonPlan(wl.shapes, wl.dtype)
+    params = WL.make_params(wl, DEV, "cpu")
+    moms = WL.make_moms(wl, DEV)
+    for s in range(2):
+        plan.step(params, WL.make_grads(wl, s, DEV, "cpu"), moms, **wl.hyper())
+    saved = ([p.cpu().clone() for p in params], [m.cpu().clone() for m in moms])
+    plan.step(params, WL.make_grads(wl, 2, DEV, "cpu"), moms, **wl.hyper())
+    torch.cuda.synchronize()
+    plan2 = MuonPlan(wl.shapes, wl.dtype)
+    p2 = [p.to(DEV) for p in saved[0]]
+    m2 = [m.to(DEV) for m in saved[1]]
+    plan2.step(p2, WL.make_grads(wl, 2, DEV, "cpu"), m2, **wl.hyper())
+    torch.cuda.synchronize()
+    for a, b in zip(params + moms, p2 + m2):
+        assert torch.equal(a, b)

@@ -214,9 +214,40 @@ class MuonPlan:
                            a, b, c, int(ns_steps), ctypes.c_void_p(workspace.data_ptr()),
                            workspace.numel(), ctypes.c_void_p(self._stream(stream))))
 
+    def bind(self, params, grads, moms, *, workspace: Optional[torch.Tensor] = None) -> "BoundStep":
+        """Validate the tensors once and keep their pointer arrays, so that
+        repeated steps over the same tensors cost one C call each."""
+        self._check_tensors(params, self.dtype, "params")
+        self._check_tensors(grads, self.dtype, "grads")
+        self._check_tensors(moms, torch.float32, "moms")
+        if workspace is None:
+            workspace = self._default_ws(params[0].device)
+        return BoundStep(self, params, grads, moms, workspace)
+
     def _default_ws(self, device) -> torch.Tensor:
         ws = getattr(self, "_ws", None)
         if ws is None or ws.device != device:
             ws = self.new_workspace(device)
             self._ws = ws
         return ws
+
+
+class BoundStep:
+    """muon_step over a fixed set of tensors (see MuonPlan.bind).  The tensors
+    are kept alive by this object; their storage must not be reallocated."""
+
+    def __init__(self, plan: MuonPlan, params, grads, moms, workspace: torch.Tensor):
+        self.plan = plan
+        self._keep = (list(params), list(grads), list(moms), workspace)
+        self._p, self._g, self._m = _ptrs(params), _ptrs(grads), _ptrs(moms)
+        self._ws = ctypes.c_void_p(workspace.data_ptr())
+        self._ws_bytes = workspace.numel()
+        self._lib = load_library()
+
+    def step(self, *, lr: float, mu: float = 0.95, nesterov: bool = True, wd: float = 0.0,
+             coeffs=(3.4445, -4.7750, 2.0315), ns_steps: int = 5, scale: float = 1.0, stream=None) -> None:
+        a, b, c = coeffs
+        _check(self._lib.muon_step(self.plan._h, self._p, self._g, self._m, self.plan._cshapes,
+                                   len(self.plan.shapes), lr, mu, 1 if nesterov else 0, wd, a, b, c,
+                                   ns_steps, scale, self._ws, self._ws_bytes,
+                                   ctypes.c_void_p(MuonPlan._stream(stream))))

@@ -3,6 +3,7 @@
 // allocated or freed here and the host never waits for the device.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -27,6 +28,17 @@ muon_status fail(muon_status s, const std::string& d) {
 }
 
 constexpr unsigned kSpinLimit = 1u << 20;  // bounded barrier wait (polls, about a second)
+
+// Distinct number per skinny launch (modulo 2^27): tags the kernel's published
+// partials, so words left by an earlier launch in the same workspace are never
+// mistaken for new ones.
+std::atomic<uint32_t> g_epoch{1};
+
+uint32_t next_epoch() {
+  uint32_t e = g_epoch.fetch_add(1) & ((1u << 27) - 1);
+  if (e == 0) e = g_epoch.fetch_add(1) & ((1u << 27) - 1);  // tag 0 marks unwritten words
+  return e;
+}
 
 // Co-resident workgroup capacity of the skinny kernel, per device id.
 std::mutex g_cap_mu;
@@ -117,6 +129,7 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         a.part = (float*)(ws + P.ws_dyn_off);
         a.sync = (uint32_t*)(ws + P.ws_sync_off);
         a.spin_limit = kSpinLimit;
+        a.epoch = next_epoch();
         e = run_skinny(a, st);
       } else {
         LargeArgs a;

@@ -105,6 +105,12 @@ __device__ __forceinline__ void buf_st_f32(rsrc_t r, uint32_t off, float v) {
 __device__ __forceinline__ void buf_st_u16(rsrc_t r, uint32_t off, uint16_t v) {
   __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
 }
+__device__ __forceinline__ u32x4 buf_ld_b128(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_st_b128(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
 
 // Hides a value from the optimiser so that an expression computed from it is
 // not merged with an identical one far away (which would keep the result

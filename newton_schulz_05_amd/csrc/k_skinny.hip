@@ -3,26 +3,34 @@
 // HyperParallel FSDP Muon optimizer RFC.
 //
 // Every matrix is split into S column slabs, one workgroup per slab.  A
-// workgroup keeps its slab of the NS iterate X in registers for the whole
-// step, so HBM sees only the compulsory traffic: G and M read, M written,
-// W read and written.  Per NS step the only data exchanged between the
-// workgroups of one matrix is their partial Gram matrix X_slab X_slab^T
-// (m x m fp32), published to the workspace and combined after a per-matrix
-// barrier.  Each workgroup then forms the same A and P = aI + bA + cA^2
-// (all fp32, fixed summation order) and applies P to its own columns.
+// workgroup keeps its slab of X0 = U (the NS input, before normalisation) in
+// registers for the whole step, so HBM sees only the compulsory traffic:
+// G and M read, M written, W read and written.
 //
-// Arithmetic: X is held in bf16 between steps; the Gram uses bf16 MFMA with
-// fp32 accumulation (exact products); P is split into bf16 hi + lo parts so
-// the apply X' = P X is accurate to about 16 mantissa bits of P; the last
-// step's result O stays fp32 up to the weight update.
+// NS runs in Gram space.  Every iterate is X_k = Q_k X0 with Q_k a
+// polynomial in A0 = X0 X0^T, so all the matrices below commute and
+//   A_k = X_k X_k^T = Q_k A0 Q_k,   P_k = a I + b A_k + c A_k^2,
+//   Q_{k+1} = P_k Q_k,              A_{k+1} = P_k A_k P_k,
+// with Q_0 = s I and A_0 = s^2 X0 X0^T (s = 1 / (||U||_F + eps)).  In exact
+// arithmetic O = Q_K X0 is the NS result of the oracle.  For m <= 32 the m x m
+// recurrences cost nothing next to the m x n products, so a step needs ONE
+// Gram of X0 (a single exchange of slab partials between the workgroups of a
+// matrix) and ONE apply O = Q_K X0, instead of one Gram, one exchange and one
+// apply per NS iteration.  The m x m arithmetic is fp32 throughout (no bf16
+// rounding of an iterate), which is also more accurate than iterating on a
+// bf16 X.
+//
+// Arithmetic: X0 is held in bf16; the Gram uses bf16 MFMA with fp32
+// accumulation (exact products); Q_K is split into bf16 hi + lo parts so the
+// apply is accurate to about 16 mantissa bits of Q_K; O stays fp32 up to the
+// weight update.
 //
 // Register layout (wave64, MFMA 32x32x16): a "block" is 32 columns of the
 // slab.  Lane l (h = l / 32, c = l % 32) holds column c of the block at the
-// 16 rows  row(r) = 8*(r/4) + 4*h + (r%4), r = 0..15.  This is the output
-// layout of the 32x32 MFMA, so the apply X' = P X maps it onto itself when
-// the contraction index is permuted the same way in P's operand: no data
-// movement between NS steps.  The Gram contracts over columns instead, so
-// each block is restaged through LDS once per step.
+// 16 rows  row(r) = 8*(r/4) + 4*h + (r%4), r = 0..15, which is the output
+// layout of the 32x32 MFMA; the apply O = Q X0 takes X0 in this layout when
+// the contraction index of Q's operand is permuted to match.  The Gram
+// contracts over columns instead, so each block is restaged through LDS.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -30,52 +38,74 @@ namespace muon {
 
 namespace {
 
-constexpr int kNB = 10;        // 32-column blocks per wave (slab <= 4 * 10 * 32 = 1280 columns)
-constexpr int kLdr = 36;       // LDS column stride (bf16) of the transpose staging
-constexpr int kPart = 1024 + 64;  // floats per published slab partial
+constexpr int kNB = 8;            // 32-column blocks per wave (slab <= 4 * 8 * 32 = 1024 columns)
+constexpr int kLdr = 36;          // LDS column stride (bf16) of the transpose staging
+constexpr int kPartW = 544;       // 8-byte words per published slab partial (upper triangle <= 528, + sum of squares)
 constexpr int kErrSlot = 2040;    // u32 index of the timeout flag in the sync region
+constexpr int kCoherent = 16;     // buffer cache policy: device-coherent access (sc1)
+constexpr int kGather = 12;       // partial words each thread has in flight while gathering
 
 __device__ __forceinline__ int row_of(int r, int h) { return ((r >> 2) << 3) + (h << 2) + (r & 3); }
-// X row that k-slot q (0..7) of k-step t holds in lane half h
-__device__ __forceinline__ int krow(int t, int h, int q) { return 16 * t + ((q >> 2) << 3) + (h << 2) + (q & 3); }
 
-// Per-matrix sense-reversing barrier among the S workgroups of matrix z.
-// sync[2z] counts arrivals, sync[2z+1] is the generation.  The wait is
-// bounded: on timeout a flag is raised and the workgroup carries on, so the
-// grid always drains.
-__device__ void matrix_barrier(uint32_t* sync, int z, int S, unsigned spin_limit) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t* cnt = sync + 2 * z;
-    uint32_t* gen = sync + 2 * z + 1;
-    const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == uint32_t(S - 1)) {
-      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      unsigned it = 0;
-      while (__hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == g0) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++it > spin_limit) {
-          __hip_atomic_store(sync + kErrSlot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  __threadfence();
+// Cross-workgroup exchange.  Every workgroup publishes its slab's partial
+// Gram (upper triangle, plus the sum of squares on the first step) as 8-byte
+// words that pair each value with a tag naming the call and the NS step.
+// The words are written and read with device-coherent accesses (they bypass
+// the per-XCD L2 write-back path), and an 8-byte word is written as a unit,
+// so a reader that sees the expected tag also sees the value: the tags are
+// the barrier, and no counter, fence or cache flush is needed.  Two parity
+// buffers suffice: a workgroup can only publish step k+2 after every
+// workgroup of its matrix has published step k+1, i.e. finished reading k.
+// Waits are bounded: on timeout a flag is raised and the workgroup carries
+// on, so the grid always drains.
+__device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
+  return uint64_t(__float_as_uint(v)) | (uint64_t(tag) << 32);
+}
+
+// i-th entry of the row-major upper triangle of an m x m matrix
+__device__ __forceinline__ void tri_ij(int e, int m, int& i, int& j) {
+  int r = 0, len = m;
+  while (e >= len) { e -= len; ++r; --len; }
+  i = r;
+  j = r + e;
 }
 
 struct SkShared {
   uint16_t stage[4][32 * kLdr];   // per-wave transpose staging, column-major [col][row]
-  float red[4][1024];             // per-wave Gram partials
-  float A[32][33];                // combined Gram (fp32)
-  uint16_t Phi[32][34], Plo[32][34];
+  // per-wave Gram partials; gathered slab partials; the m x m matrices of the
+  // Gram-space recurrence; per-wave O staging at the end
+  float red[4][32 * 33];
+  float A[32][33];
+  float mat[2][32][33];
+  u16x8 pop[2][2][64];            // Q operand registers per lane: [k-step][hi, lo][lane]
   float ss[4];
 };
+
+// C = epi(i, j, (A B)[i][j]) for 32 x 32 fp32 matrices in LDS (stride 33).
+// The four waves split the contraction: wave w runs k = 8w .. 8w+7 on the
+// fp32 MFMA (32x32x2), parks its partial product in red[w], and the four
+// partials are added in a fixed order, so every workgroup computes bitwise
+// the same C.  C may alias A or B.
+template <typename Epi>
+__device__ __forceinline__ void mm32(float (*C)[33], const float (*A)[33], const float (*B)[33],
+                                     float (*red)[32 * 33], int t, Epi epi) {
+  const int lane = t & 63, w = t >> 6, cl = lane & 31, h = lane >> 5;
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int k = 8 * w + 2 * s + h;
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(A[cl][k], B[k][cl], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[w][row_of(r, h) * 33 + cl] = acc[r];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = t + 256 * q, i = e >> 5, j = e & 31, o = i * 33 + j;
+    C[i][j] = epi(i, j, (red[0][o] + red[1][o]) + (red[2][o] + red[3][o]));
+  }
+  __syncthreads();
+}
 
 }  // namespace
 
@@ -83,7 +113,8 @@ struct SkShared {
 template <typename PT, int MODE>
 __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalars sc, int m, int64_t n,
                                                         int S, int64_t slab_w, float* __restrict__ part,
-                                                        uint32_t* __restrict__ sync, unsigned spin_limit) {
+                                                        uint32_t* __restrict__ sync, unsigned spin_limit,
+                                                        uint32_t epoch) {
   static_assert(sizeof(PT) == 2, "skinny path is bf16");
   constexpr bool step_mode = MODE == 0;
   __shared__ SkShared sh;
@@ -103,8 +134,11 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   const rsrc_t rG = make_rsrc(G, elems * 2);
   const rsrc_t rM = make_rsrc(Mm, step_mode ? elems * 4 : 0);
   const rsrc_t rW = make_rsrc(Wout, elems * (MODE == 1 ? 4 : 2));
+  // this chunk's partial buffer: [matrix][parity][slab][kPartW] 8-byte words
+  const rsrc_t rP = make_rsrc(part, uint32_t(gridDim.x) * 2u * uint32_t(kPartW) * 8u);
+  const uint32_t part_z = uint32_t(z) * 2u * uint32_t(S) * uint32_t(kPartW);  // word index
   const int v = threadIdx.x >> 6;  // wave index (uniform within the wave)
-  float* part_z = part + int64_t(z) * 2 * S * kPart;
+  const int ntri = m * (m + 1) / 2;  // published Gram entries
 
   // Thread-index-derived values are re-derived through opaque() at the top of
   // each phase: otherwise the compiler hoists every address it can out of
@@ -123,33 +157,90 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   float ss = 0.f;
 
   // ---- momentum, Nesterov, NS input --------------------------------------
+  // Wide matrices with 16-byte aligned rows take the vector path: lane
+  // (r = lane / 2, half = lane % 2) moves 16 consecutive columns of row r with
+  // 16-byte accesses, and the block is transposed to the register layout
+  // through this wave's LDS staging.  The next block's loads are issued before
+  // the current block is processed.  Other blocks use element accesses.
+  const bool vec = !tr && (nn % 8) == 0;
+  uint16_t* stg = sh.stage[v];
+  auto full = [&](int q) { return vec && c0 + (v * kNB + q) * 32 + 32 <= c1; };
+  auto row_off = [&](int q, int lane) -> uint32_t {
+    const int r = lane >> 1, hc = lane & 1;
+    return (r < m) ? uint32_t(r * nn + c0 + (v * kNB + q) * 32 + 16 * hc) : kOob;
+  };
+  u32x4 pg[2][2], pm[2][4];  // prefetched G and M of a block (ping-pong by block parity)
+  auto issue = [&](int q) {
+    const uint32_t e0 = row_off(q, opaque(int(threadIdx.x)) & 63);
+    pg[q & 1][0] = buf_ld_b128(rG, e0 * 2);
+    pg[q & 1][1] = buf_ld_b128(rG, e0 * 2 + 16);
+    if (step_mode) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pm[q & 1][i] = buf_ld_b128(rM, e0 * 4 + 16 * i);
+    }
+  };
+  if (full(0)) issue(0);
 #pragma unroll
   for (int q = 0; q < kNB; ++q) {
-    const int lane = opaque(int(threadIdx.x)) & 63, h = lane >> 5;
-    const int col = c0 + (v * kNB + q) * 32 + (lane & 31);
-    // all loads of the block first (stores to M below could alias later
-    // loads as far as the compiler knows), then the arithmetic and stores
-    uint32_t e[16];
-    float gv[16], mv[16], uu[16];
+    if (q + 1 < kNB && full(q + 1)) issue(q + 1);
+    const int lane = opaque(int(threadIdx.x)) & 63, h = lane >> 5, cl = lane & 31;
+    if (full(q)) {
+      const int r = lane >> 1, hc = lane & 1;
+      const uint32_t e0 = row_off(q, lane);
+      float gv[16], u[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      e[r] = eoff(row_of(r, h), col);
-      gv[r] = bf2f(buf_ld_u16(rG, e[r] * 2));
-      if (step_mode) mv[r] = buf_ld_f32(rM, e[r] * 4);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float u = gv[r];
-      if (step_mode) {
-        const float mn = fmaf(sc.mu, mv[r], gv[r]);
-        buf_st_f32(rM, e[r] * 4, mn);
-        u = sc.nesterov ? fmaf(sc.mu, mn, gv[r]) : mn;
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t w = pg[q & 1][j >> 2][j & 3];
+        gv[2 * j] = bf2f(uint16_t(w & 0xffffu));
+        gv[2 * j + 1] = bf2f(uint16_t(w >> 16));
       }
-      ss = fmaf(u, u, ss);  // padding reads 0, adds nothing
-      uu[r] = u;
-    }
 #pragma unroll
-    for (int d = 0; d < 8; ++d) xw[q][d] = f2bf2(uu[2 * d], uu[2 * d + 1]);
+      for (int j = 0; j < 16; ++j) {
+        u[j] = gv[j];
+        if (step_mode) {
+          const float mn = fmaf(sc.mu, __uint_as_float(pm[q & 1][j >> 2][j & 3]), gv[j]);
+          pm[q & 1][j >> 2][j & 3] = __float_as_uint(mn);
+          u[j] = sc.nesterov ? fmaf(sc.mu, mn, gv[j]) : mn;
+        }
+        ss = fmaf(u[j], u[j], ss);  // padding rows read 0 and add nothing
+      }
+      if (step_mode) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) buf_st_b128(rM, e0 * 4 + 16 * i, pm[q & 1][i]);
+      }
+      // stage column-major [col][row] (bf16), then read the register layout
+#pragma unroll
+      for (int j = 0; j < 16; ++j) stg[(16 * hc + j) * kLdr + r] = f2bf(u[j]);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int d = 0; d < 8; ++d) xw[q][d] = *(const uint32_t*)(stg + cl * kLdr + row_of(2 * d, h));
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      const int col = c0 + (v * kNB + q) * 32 + cl;
+      // all loads of the block first (stores to M below could alias later
+      // loads as far as the compiler knows), then the arithmetic and stores
+      uint32_t e[16];
+      float gv[16], mv[16], uu[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        e[r] = eoff(row_of(r, h), col);
+        gv[r] = bf2f(buf_ld_u16(rG, e[r] * 2));
+        if (step_mode) mv[r] = buf_ld_f32(rM, e[r] * 4);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float u = gv[r];
+        if (step_mode) {
+          const float mn = fmaf(sc.mu, mv[r], gv[r]);
+          buf_st_f32(rM, e[r] * 4, mn);
+          u = sc.nesterov ? fmaf(sc.mu, mn, gv[r]) : mn;
+        }
+        ss = fmaf(u, u, ss);
+        uu[r] = u;
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) xw[q][d] = f2bf2(uu[2 * d], uu[2 * d + 1]);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -158,7 +249,6 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   // wave's LDS area, read it back row-per-lane, one MFMA per 16 columns.
   auto gram_block = [&](const uint32_t* x, f32x16& gacc, int lane) {
     const int h = lane >> 5, cl = lane & 31;
-    uint16_t* stg = sh.stage[v];
 #pragma unroll
     for (int g = 0; g < 4; ++g) *(u32x2*)(stg + cl * kLdr + 8 * g + 4 * h) = u32x2{x[2 * g], x[2 * g + 1]};
 #pragma unroll
@@ -171,96 +261,204 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
     }
   };
 
-  // combine the 4 wave partials and publish this slab's partial
-  auto publish = [&](const f32x16& gacc, int par, bool with_ss) {
+  // combine the 4 wave partials and publish this slab's partial for NS step
+  // k: upper triangle of the Gram, then (first step) the sum of squares
+  auto publish = [&](const f32x16& gacc, int k, bool with_ss) {
     const int t = opaque(int(threadIdx.x)), lane = t & 63, h = lane >> 5, cl = lane & 31;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sh.red[v][row_of(r, h) * 32 + cl] = gacc[r];
     float tot = 0.f;
     if (with_ss) tot = block_sum_256(ss, sh.ss);  // contains __syncthreads
     __syncthreads();
-    float* dst = part_z + (int64_t(par) * S + s) * kPart;
-    for (int e = t; e < m * m; e += 256) {
-      const int i = e / m, j = e - i * m;
+    const uint32_t tag = (epoch << 5) | uint32_t(k + 1);
+    const uint32_t dst = part_z + (uint32_t(k & 1) * S + s) * kPartW;
+    for (int e = t; e < ntri; e += 256) {
+      int i, j;
+      tri_ij(e, m, i, j);
       const int o = i * 32 + j;
-      dst[e] = (sh.red[0][o] + sh.red[1][o]) + (sh.red[2][o] + sh.red[3][o]);
+      const float val = (sh.red[0][o] + sh.red[1][o]) + (sh.red[2][o] + sh.red[3][o]);
+      const uint64_t w = tagged(val, tag);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), rP, int((dst + e) * 8), 0, kCoherent);
     }
-    if (with_ss && t == 0) dst[1024] = tot;
+    if (with_ss && t == 0) {
+      const uint64_t w = tagged(tot, tag);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), rP, int((dst + 528) * 8), 0, kCoherent);
+    }
   };
 
-  // after the barrier: combine all slab partials (fixed order) into A and
-  // form P = ps * (aI + bA + cA^2) with its hi/lo split; on the first step
-  // also the normalisation (A = s^2 * sum, ps = s)
-  auto form_p = [&](int par, bool first, float& s_out) {
+  // Gather the slab partials once their tags show up and combine them in
+  // slab order (identical in every workgroup): sh.A = s^2 * X0 X0^T (padded
+  // with zeros to 32 x 32) and s_out = s.
+  auto gather_a = [&](int k, bool first, float& s_out) {
     const int t = opaque(int(threadIdx.x));
-    const float* src = part_z + int64_t(par) * S * kPart;
-    float s2 = 1.f, ps = 1.f;
+    const uint32_t tag = (epoch << 5) | uint32_t(k + 1);
+    const uint32_t src = part_z + uint32_t(k & 1) * S * kPartW;
+    // words per slab: the triangle, plus the sum of squares on the first step
+    const int nw = ntri + (first ? 1 : 0);
+    // The per-wave staging area (free between publish and the last apply)
+    // holds `per` slabs of words at a time.  Each thread has up to kGather
+    // loads in flight, then waits for their tags and parks the values in LDS.
+    float* gbuf = &sh.red[0][0];
+    const int per = min(S, min(4 * 32 * 33, 256 * kGather) / nw);
+    float acc[3] = {0.f, 0.f, 0.f};  // this thread's entries t, t+256, t+512
+    for (int q0 = 0; q0 < S; q0 += per) {
+      const int nq = min(per, S - q0);
+      const int tot = nq * nw;
+      auto woff = [&](int j) -> uint32_t {
+        const int idx = t + 256 * j;
+        const int q = idx / nw, e = idx - q * nw;
+        return (idx < tot) ? (src + (q0 + q) * kPartW + (e < ntri ? e : 528)) * 8 : kOob * 8;
+      };
+      u32x2 w[kGather];
+#pragma unroll
+      for (int j = 0; j < kGather; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b64(rP, int(woff(j)), 0, kCoherent);
+      unsigned it = 0;
+      for (;;) {
+        bool ready = true;
+#pragma unroll
+        for (int j = 0; j < kGather; ++j) ready &= (t + 256 * j >= tot) || (w[j][1] == tag);
+        if (ready) break;
+        if (++it > spin_limit) {
+          __hip_atomic_store(sync + kErrSlot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int j = 0; j < kGather; ++j)
+          if (t + 256 * j < tot && w[j][1] != tag) w[j] = __builtin_amdgcn_raw_buffer_load_b64(rP, int(woff(j)), 0, kCoherent);
+      }
+#pragma unroll
+      for (int j = 0; j < kGather; ++j)
+        if (t + 256 * j < tot) gbuf[t + 256 * j] = __uint_as_float(w[j][0]);
+      __syncthreads();
+      // fixed slab order within and across rounds
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        const int e = t + 256 * r;
+        if (e < nw)
+          for (int q = 0; q < nq; ++q) acc[r] += gbuf[q * nw + e];
+      }
+      __syncthreads();
+    }
+    float s2 = 1.f;
     if (first) {
-      float tot = 0.f;
-      for (int q = 0; q < S; ++q) tot += src[int64_t(q) * kPart + 1024];
-      const float sn = 1.0f / (sqrtf(tot) + kNsEps);
+      // word ntri (the sum of squares) is entry ntri: broadcast it via LDS
+      if (t == ntri % 256) sh.ss[0] = acc[ntri / 256];
+      __syncthreads();
+      const float sn = 1.0f / (sqrtf(sh.ss[0]) + kNsEps);
       s2 = sn * sn;
-      ps = sn;
       s_out = sn;
     }
-    for (int e = t; e < 1024; e += 256) {
-      const int i = e >> 5, j = e & 31;
-      float a = 0.f;
-      if (i < m && j < m) {
-        for (int q = 0; q < S; ++q) a += src[int64_t(q) * kPart + i * m + j];
-        a *= s2;
-      }
-      sh.A[i][j] = a;
-    }
+    // zero the padded A, then fill both triangles
+    for (int e = t; e < 32 * 33; e += 256) (&sh.A[0][0])[e] = 0.f;
     __syncthreads();
-    for (int e = t; e < 1024; e += 256) {
-      const int i = e >> 5, j = e & 31;
-      float p = 0.f;
-      if (i < m && j < m) {
-        float a2 = 0.f;
-        for (int k = 0; k < m; ++k) a2 = fmaf(sh.A[i][k], sh.A[k][j], a2);
-        p = fmaf(sc.c, a2, sc.b * sh.A[i][j]);
-        if (i == j) p += sc.a;
-        p *= ps;
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const int e = t + 256 * r;
+      if (e < ntri) {
+        int i, j;
+        tri_ij(e, m, i, j);
+        sh.A[i][j] = acc[r] * s2;
+        sh.A[j][i] = acc[r] * s2;
       }
-      const uint16_t ph = f2bf(p);
-      sh.Phi[i][j] = ph;
-      sh.Plo[i][j] = f2bf(p - bf2f(ph));
     }
     __syncthreads();
   };
 
-  // this lane's operand registers of P (hi, lo) for the two k-steps: the
-  // contraction index is permuted to match the row layout of X
-  u16x8 ph[2], pl[2];
-  auto load_p = [&]() {
-    const int lane = opaque(int(threadIdx.x)) & 63, h = lane >> 5, cl = lane & 31;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int kr = krow(tt, h, q);
-        ph[tt][q] = sh.Phi[cl][kr];
-        pl[tt][q] = sh.Plo[cl][kr];
+  // Gram-space NS: from sh.A = A0 and s, run the recurrence and leave Q_K
+  // (hi/lo bf16) in the per-lane MFMA operand layout sh.pop.
+  auto gram_space_ns = [&](float snorm) {
+    const int t = opaque(int(threadIdx.x));
+    float (*A)[33] = sh.A;
+    float (*P)[33] = sh.mat[0];
+    float (*T)[33] = sh.mat[1];
+    // Q and its successor live in the (now idle) transpose staging area
+    float (*Q)[33] = (float (*)[33])(void*)&sh.stage[0][0];
+    float (*Qn)[33] = Q + 32;
+    float (*red)[32 * 33] = sh.red;
+    for (int e = t; e < 32 * 33; e += 256) {
+      const int i = e / 33, j = e - i * 33;
+      (&Q[0][0])[e] = (i == j && i < m) ? snorm : 0.f;
+    }
+    __syncthreads();
+    const float ca = sc.a, cb = sc.b, cc = sc.c;
+    const int mm = m;
+    auto ident = [](int, int, float v) { return v; };
+    const int steps = sc.ns_steps;
+    for (int k = 0; k < steps; ++k) {
+      // P = a I + b A + c A^2
+      mm32(P, A, A, red, t, [=](int i, int j, float a2) {
+        float p = fmaf(cc, a2, cb * A[i][j]);
+        return (i == j && i < mm) ? p + ca : p;
+      });
+      mm32(Qn, P, Q, red, t, ident);  // Q <- P Q
+      { float (*tq)[33] = Q; Q = Qn; Qn = tq; }
+      if (k + 1 < steps) {
+        mm32(T, P, A, red, t, ident);  // A <- P A P
+        mm32(A, T, P, red, t, ident);
       }
+    }
+    // Q (fp32) -> hi/lo bf16 operand registers: Q[i][kr] is k-slot q of lane
+    // (h, i) in k-step tt, where X0 row kr sits at k-slot q of lane half h
+    for (int e = t; e < 32 * 32; e += 256) {
+      const int i = e >> 5, kr = e & 31;
+      const float qv = Q[i][kr];
+      const uint16_t hi = f2bf(qv);
+      const int tt = kr >> 4, hh = (kr >> 2) & 1, q = ((kr >> 3) & 1) * 4 + (kr & 3);
+      sh.pop[tt][0][hh * 32 + i][q] = hi;
+      sh.pop[tt][1][hh * 32 + i][q] = f2bf(qv - bf2f(hi));
+    }
+    __syncthreads();
   };
-  auto apply = [&](const uint32_t* x) {
+
+  auto apply = [&](const uint32_t* x, int lane) {
     const bf16x8 x0 = __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], x[2], x[3]});
     const bf16x8 x1 = __builtin_bit_cast(bf16x8, u32x4{x[4], x[5], x[6], x[7]});
     f32x16 acc = f32x16{};
-    acc = mfma32x32x16(as_bf16x8(ph[0]), x0, acc);
-    acc = mfma32x32x16(as_bf16x8(pl[0]), x0, acc);
-    acc = mfma32x32x16(as_bf16x8(ph[1]), x1, acc);
-    acc = mfma32x32x16(as_bf16x8(pl[1]), x1, acc);
+    acc = mfma32x32x16(as_bf16x8(sh.pop[0][0][lane]), x0, acc);
+    acc = mfma32x32x16(as_bf16x8(sh.pop[0][1][lane]), x0, acc);
+    acc = mfma32x32x16(as_bf16x8(sh.pop[1][0][lane]), x1, acc);
+    acc = mfma32x32x16(as_bf16x8(sh.pop[1][1][lane]), x1, acc);
     return acc;
   };
 
-  // O for one block (16 values per lane) -> fp32 store or weight update;
-  // all W loads are issued before the stores
+  // O for one block (16 values per lane) -> fp32 store or weight update
   const float keep = 1.0f - sc.lr * sc.wd, stepc = -sc.lr * sc.scale;
   auto emit_block = [&](const f32x16& o, int q) {
-    const int lane = opaque(int(threadIdx.x)) & 63, h = lane >> 5;
-    const int col = c0 + (v * kNB + q) * 32 + (lane & 31);
+    const int lane = opaque(int(threadIdx.x)) & 63, h = lane >> 5, cl = lane & 31;
+    if (full(q)) {
+      // O through LDS (fp32, column-major, stride 33) to row-major vectors
+      float* fst = sh.red[v];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) fst[cl * 33 + row_of(r, h)] = o[r];
+      __builtin_amdgcn_wave_barrier();
+      const int r = lane >> 1, hc = lane & 1;
+      float ov[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ov[j] = fst[(16 * hc + j) * 33 + r];
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t e0 = row_off(q, lane);
+      if (!step_mode) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          buf_st_b128(rW, e0 * 4 + 16 * i, u32x4{__float_as_uint(ov[4 * i]), __float_as_uint(ov[4 * i + 1]),
+                                                 __float_as_uint(ov[4 * i + 2]), __float_as_uint(ov[4 * i + 3])});
+      } else {
+        const u32x4 wa = buf_ld_b128(rW, e0 * 2), wb = buf_ld_b128(rW, e0 * 2 + 16);
+        u32x4 na, nb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w = (j < 4) ? wa[j] : wb[j - 4];
+          const float lo = fmaf(stepc, ov[2 * j], bf2f(uint16_t(w & 0xffffu)) * keep);
+          const float hi = fmaf(stepc, ov[2 * j + 1], bf2f(uint16_t(w >> 16)) * keep);
+          if (j < 4) na[j] = f2bf2(lo, hi); else nb[j - 4] = f2bf2(lo, hi);
+        }
+        buf_st_b128(rW, e0 * 2, na);
+        buf_st_b128(rW, e0 * 2 + 16, nb);
+      }
+      return;
+    }
+    const int col = c0 + (v * kNB + q) * 32 + cl;
     uint32_t e[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) e[r] = eoff(row_of(r, h), col);
@@ -276,59 +474,22 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
     }
   };
 
-  // ---- Gram of X0 -----------------------------------------------------------
+  // ---- Gram of X0, one exchange, Gram-space NS, apply and update ------------
   f32x16 gacc = f32x16{};
   {
     const int lane = opaque(int(threadIdx.x)) & 63;
 #pragma unroll
     for (int q = 0; q < kNB; ++q) gram_block(xw[q], gacc, lane);
   }
-
-  const int steps = sc.ns_steps;
+  publish(gacc, 0, true);
   float snorm = 1.f;
-
-  if (steps == 0) {
-    publish(gacc, 0, true);
-    matrix_barrier(sync, z, S, spin_limit);
-    form_p(0, true, snorm);
-#pragma unroll
-    for (int q = 0; q < kNB; ++q) {
-      f32x16 o;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[r] = snorm * bf2f(uint16_t(xw[q][r >> 1] >> (16 * (r & 1))));
-      emit_block(o, q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return;
-  }
-
-  for (int k = 0; k < steps - 1; ++k) {
-    const int par = k & 1;
-    publish(gacc, par, k == 0);
-    matrix_barrier(sync, z, S, spin_limit);
-    form_p(par, k == 0, snorm);
-    load_p();
-    gacc = f32x16{};
+  gather_a(0, true, snorm);
+  gram_space_ns(snorm);
+  {
     const int lane = opaque(int(threadIdx.x)) & 63;
 #pragma unroll
     for (int q = 0; q < kNB; ++q) {
-      const f32x16 acc = apply(xw[q]);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) xw[q][d] = f2bf2(acc[2 * d], acc[2 * d + 1]);
-      gram_block(xw[q], gacc, lane);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // last NS step: O = P X in fp32, then the update
-  {
-    const int k = steps - 1;
-    publish(gacc, k & 1, k == 0);
-    matrix_barrier(sync, z, S, spin_limit);
-    form_p(k & 1, k == 0, snorm);
-    load_p();
-#pragma unroll
-    for (int q = 0; q < kNB; ++q) {
-      const f32x16 acc = apply(xw[q]);
+      const f32x16 acc = apply(xw[q], lane);
       emit_block(acc, q);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -339,10 +500,10 @@ hipError_t run_skinny(const SkinnyArgs& g, hipStream_t st) {
   const unsigned grid = unsigned(g.count * g.slabs);
   if (g.sc.mode == 0)
     hipLaunchKernelGGL((skinny_kernel<uint16_t, 0>), dim3(grid), dim3(256), 0, st, g.tab, g.sc, g.m, g.n,
-                       g.slabs, g.slab_w, g.part, g.sync, g.spin_limit);
+                       g.slabs, g.slab_w, g.part, g.sync, g.spin_limit, g.epoch);
   else
     hipLaunchKernelGGL((skinny_kernel<uint16_t, 1>), dim3(grid), dim3(256), 0, st, g.tab, g.sc, g.m, g.n,
-                       g.slabs, g.slab_w, g.part, g.sync, g.spin_limit);
+                       g.slabs, g.slab_w, g.part, g.sync, g.spin_limit, g.epoch);
   return hipGetLastError();
 }
 

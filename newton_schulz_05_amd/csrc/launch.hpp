@@ -29,8 +29,9 @@ struct SkinnyArgs {
   int slabs;
   int64_t slab_w;
   float* part;       // published slab partials
-  uint32_t* sync;    // barrier counters (zero between calls)
+  uint32_t* sync;    // timeout flag
   unsigned spin_limit;
+  uint32_t epoch;    // distinct per call: tags the published partials
 };
 
 hipError_t run_large(const LargeArgs& a, hipStream_t st);

@@ -26,9 +26,9 @@ enum Path : int32_t {
 
 // Geometry constants the kernels are compiled for.
 constexpr int64_t kSkinnyMaxM = 32;          // rows of the padded MFMA tile
-constexpr int64_t kSkinnyBlocksPerWave = 10; // 32-column blocks each wave keeps in registers
+constexpr int64_t kSkinnyBlocksPerWave = 8;  // 32-column blocks each wave keeps in registers
 constexpr int64_t kSkinnyWaves = 4;
-constexpr int64_t kSkinnyMaxSlab = 32 * kSkinnyBlocksPerWave * kSkinnyWaves;  // 1280 columns
+constexpr int64_t kSkinnyMaxSlab = 32 * kSkinnyBlocksPerWave * kSkinnyWaves;  // 1024 columns
 constexpr int64_t kSkinnyCapacity = 768;     // co-resident workgroups assumed (3 per CU x 256 CUs)
 constexpr int64_t kSkinnyPartStride = 1024 + 64;  // floats per slab partial (32x32 Gram + sum of squares)
 constexpr int64_t kMfmaTile = 128;           // row/column padding of the MFMA path

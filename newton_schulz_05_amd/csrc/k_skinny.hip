@@ -82,27 +82,25 @@ struct SkShared {
 };
 
 // C = epi(i, j, (A B)[i][j]) for 32 x 32 fp32 matrices in LDS (stride 33).
-// The four waves split the contraction: wave w runs k = 8w .. 8w+7 on the
-// fp32 MFMA (32x32x2), parks its partial product in red[w], and the four
-// partials are added in a fixed order, so every workgroup computes bitwise
-// the same C.  C may alias A or B.
+// Wave w computes the 16 x 16 quadrant (w / 2, w % 2) of C over the whole
+// contraction with the fp32 MFMA (16x16x4, fixed k order), so every
+// workgroup computes bitwise the same C.  C may alias A or B.
 template <typename Epi>
-__device__ __forceinline__ void mm32(float (*C)[33], const float (*A)[33], const float (*B)[33],
-                                     float (*red)[32 * 33], int t, Epi epi) {
-  const int lane = t & 63, w = t >> 6, cl = lane & 31, h = lane >> 5;
-  f32x16 acc = f32x16{};
+__device__ __forceinline__ void mm32(float (*C)[33], const float (*A)[33], const float (*B)[33], int t,
+                                     Epi epi) {
+  const int lane = t & 63, w = t >> 6;
+  const int r0 = (w >> 1) * 16, c0 = (w & 1) * 16, l16 = lane & 15, l4 = lane >> 4;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int k = 8 * w + 2 * s + h;
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(A[cl][k], B[k][cl], acc, 0, 0, 0);
+  for (int s = 0; s < 8; ++s) {
+    const int k = 4 * s + l4;
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r0 + l16][k], B[k][c0 + l16], acc, 0, 0, 0);
   }
+  __syncthreads();  // every operand read is done before C is overwritten
 #pragma unroll
-  for (int r = 0; r < 16; ++r) red[w][row_of(r, h) * 33 + cl] = acc[r];
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = t + 256 * q, i = e >> 5, j = e & 31, o = i * 33 + j;
-    C[i][j] = epi(i, j, (red[0][o] + red[1][o]) + (red[2][o] + red[3][o]));
+  for (int r = 0; r < 4; ++r) {
+    const int i = r0 + 4 * l4 + r, j = c0 + l16;
+    C[i][j] = epi(i, j, acc[r]);
   }
   __syncthreads();
 }
@@ -343,7 +341,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
     float s2 = 1.f;
     if (first) {
       // word ntri (the sum of squares) is entry ntri: broadcast it via LDS
-      if (t == ntri % 256) sh.ss[0] = acc[ntri / 256];
+      if (t == ntri % 256) sh.ss[0] = (ntri < 256) ? acc[0] : (ntri < 512) ? acc[1] : acc[2];
       __syncthreads();
       const float sn = 1.0f / (sqrtf(sh.ss[0]) + kNsEps);
       s2 = sn * sn;
@@ -375,7 +373,6 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
     // Q and its successor live in the (now idle) transpose staging area
     float (*Q)[33] = (float (*)[33])(void*)&sh.stage[0][0];
     float (*Qn)[33] = Q + 32;
-    float (*red)[32 * 33] = sh.red;
     for (int e = t; e < 32 * 33; e += 256) {
       const int i = e / 33, j = e - i * 33;
       (&Q[0][0])[e] = (i == j && i < m) ? snorm : 0.f;
@@ -387,15 +384,15 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
     const int steps = sc.ns_steps;
     for (int k = 0; k < steps; ++k) {
       // P = a I + b A + c A^2
-      mm32(P, A, A, red, t, [=](int i, int j, float a2) {
+      mm32(P, A, A, t, [=](int i, int j, float a2) {
         float p = fmaf(cc, a2, cb * A[i][j]);
         return (i == j && i < mm) ? p + ca : p;
       });
-      mm32(Qn, P, Q, red, t, ident);  // Q <- P Q
+      mm32(Qn, P, Q, t, ident);  // Q <- P Q
       { float (*tq)[33] = Q; Q = Qn; Qn = tq; }
       if (k + 1 < steps) {
-        mm32(T, P, A, red, t, ident);  // A <- P A P
-        mm32(A, T, P, red, t, ident);
+        mm32(T, P, A, t, ident);  // A <- P A P
+        mm32(A, T, P, t, ident);
       }
     }
     // Q (fp32) -> hi/lo bf16 operand registers: Q[i][kr] is k-slot q of lane

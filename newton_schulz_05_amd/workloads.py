@@ -98,3 +98,16 @@ def make_grads(wl: Workload, step: int, device, gen_device=None) -> List[torch.T
 
 def make_moms(wl: Workload, device) -> List[torch.Tensor]:
     return [torch.zeros(tuple(s), dtype=torch.float32, device=device) for s in wl.shapes]
+
+
+def numpy_normal(shape, seed: int, std: float, dtype: torch.dtype) -> torch.Tensor:
+    """Host-side draw with NumPy's PCG64 generator (integer arithmetic, so the
+    values are the same on every machine), rounded to `dtype`.  Used where a
+    stored expected value must be reproduced on another host."""
+    import numpy as np
+
+    rng = np.random.Generator(np.random.PCG64(int(seed)))
+    x = rng.standard_normal(tuple(shape), dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return torch.from_numpy(x).to(dtype)

@@ -142,6 +142,7 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         a.n = grp.n;
         a.mp = grp.mp;
         a.np = grp.np;
+        a.tile = grp.tile;
         a.bf16 = (grp.path == PATH_MFMA);
         e = run_large(a, st);
       }

@@ -284,106 +284,154 @@ __device__ __forceinline__ void tile_coords(int t, int T, bool upper, int& ti, i
 
 // ============================================================================
 // bf16 MFMA GEMM, "NT": C[i][j] = sum_k A[i][k] * B[j][k] (+ split products)
-// A, B row-major with k contiguous; all dims padded to the tile sizes.
-// 128x128 output tile per block of 256 threads (2x2 waves of 64x64), BK = 64,
-// LDS double buffered, 16-byte chunks XOR-swizzled by row.
-// NPROD = 1: C = A B^T.   NPROD = 3: C = Ah Bh^T + Ah Bl^T + Al Bh^T.
+// A, B row-major with k contiguous; all dims padded to the tile size.
+//
+// TILE x TILE output tile per block: 256 -> 8 waves (2 x 4) of 128 x 64,
+// 128 -> 4 waves (2 x 2) of 64 x 64; 32x32x16 MFMAs.  Operand tiles go from
+// global memory straight into LDS (global_load_lds, 16 bytes a lane), two
+// stages, so no VGPRs are spent on staging.  Each 16-byte chunk of a row
+// sits at chunk index (c ^ g(row)) so that the fragment reads (32 rows x 2
+// chunks per instruction) hit distinct banks:
+//   BK = 64 (8 chunks a row): g(r) = (r & 7) ^ ((r >> 3) & 3)
+//   BK = 32 (4 chunks a row): g(r) = ((r >> 1) ^ (r >> 3)) & 3
+// NPROD = 1: C = A B^T (BK = 64).
+// NPROD = 3: C = Ah Bh^T + Ah Bl^T + Al Bh^T (four operand planes, BK = 32,
+//            so the LDS footprint matches).
+// Per 16-wide k slice every output element takes its MFMA products in the
+// same order whatever TILE is, and zero padding adds exact zeros, so the two
+// tile sizes give bitwise identical results.
 // ============================================================================
-constexpr int GB_M = 128, GB_N = 128, GB_K = 64;
+template <int TILE>
+struct GemmGeom {
+  static constexpr int NT = (TILE == 256) ? 512 : 256;
+  static constexpr int WN = (TILE == 256) ? 4 : 2;
+  static constexpr int WM = 2;
+  static constexpr int TMW = TILE / WM, TNW = TILE / WN;
+  static constexpr int FM = TMW / 32, FN = TNW / 32;
+  static constexpr int MIN_BLOCKS = (TILE == 256) ? 1 : 2;
+};
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// 16 bytes per lane from global memory into LDS; lane l writes lds_base + 16 l
+__device__ __forceinline__ void dma16(const uint16_t* src, u16x8* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
 
-template <int NPROD, typename Epi>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
+template <int CPR>
+__device__ __forceinline__ int chunk_swz(int row) {
+  if constexpr (CPR == 8) return (row & 7) ^ ((row >> 3) & 3);
+  else return ((row >> 1) ^ (row >> 3)) & 3;
+}
+
+template <int TILE, int NPROD, typename Epi>
+__global__ __launch_bounds__(TILE == 256 ? 512 : 256, TILE == 256 ? 1 : 2) void gemm_bf16_kernel(
     const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al, int64_t lda, int64_t sA,
     const uint16_t* __restrict__ Bh, const uint16_t* __restrict__ Bl, int64_t ldb, int64_t sB,
     int64_t K, int tilesN, int upper, Epi epi) {
-  constexpr int NA = (NPROD == 3) ? 2 : 1;   // operand planes per side
-  __shared__ u16x8 lds[2][NA * 2][GB_M * GB_K / 8];  // [stage][plane: Ah, (Al), Bh, (Bl)]
+  using G = GemmGeom<TILE>;
+  constexpr int NA = (NPROD == 3) ? 2 : 1;      // operand planes per side
+  constexpr int BK = (NPROD == 3) ? 32 : 64;
+  constexpr int CPR = BK / 8;                   // 16-byte chunks per row
+  constexpr int PLANE = TILE * CPR;             // chunks per operand plane
+  constexpr int NW = G::NT / 64;
+  constexpr int LP = PLANE / G::NT;             // loads per thread per plane
+  constexpr int KS = BK / 16;
+  __shared__ u16x8 lds[2][2 * NA][PLANE];       // [stage][Ah, (Al), Bh, (Bl)]
   const int z = blockIdx.y;
   int ti, tj;
   tile_coords(blockIdx.x, tilesN, upper != 0, ti, tj);
-  const int64_t row0 = int64_t(ti) * GB_M, col0 = int64_t(tj) * GB_N;
-  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-  const int wr = (wid >> 1) * 64, wc = (wid & 1) * 64;
+  const int64_t row0 = int64_t(ti) * TILE, col0 = int64_t(tj) * TILE;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int wr = (wv / G::WN) * G::TMW, wc = (wv % G::WN) * G::TNW;
 
-  const uint16_t* gA[NA];
-  const uint16_t* gB[NA];
-  gA[0] = Ah + int64_t(z) * sA + row0 * lda;
-  gB[0] = Bh + int64_t(z) * sB + col0 * ldb;
-  if (NA == 2) {
-    gA[NA - 1] = Al + int64_t(z) * sA + row0 * lda;
-    gB[NA - 1] = Bl + int64_t(z) * sB + col0 * ldb;
+  const uint16_t* gsrc[2 * NA];
+  gsrc[0] = Ah + int64_t(z) * sA + row0 * lda;
+  gsrc[NA] = Bh + int64_t(z) * sB + col0 * ldb;
+  if constexpr (NA == 2) {
+    gsrc[1] = Al + int64_t(z) * sA + row0 * lda;
+    gsrc[3] = Bl + int64_t(z) * sB + col0 * ldb;
   }
 
-  f32x16 acc[2][2];
+  f32x16 acc[G::FM][G::FN];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < G::FM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < G::FN; ++b) acc[a][b] = f32x16{};
 
-  u16x8 ra[NA][4], rb[NA][4];
-  auto gload = [&](int64_t k0) {
+  // wave w's p-th load of a plane fills chunks [(p*NW + w)*64, +64): lane l
+  // takes chunk c = (p*NW + w)*64 + l, i.e. row c / CPR, stored position
+  // c % CPR, which holds logical chunk (c % CPR) ^ g(row)
+  auto gload = [&](int64_t k0, int st) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int q = t + 256 * p, r = q >> 3, ch = q & 7;
+    for (int s = 0; s < 2 * NA; ++s) {
+      const int64_t ld = (s < NA) ? lda : ldb;
 #pragma unroll
-      for (int s = 0; s < NA; ++s) {
-        ra[s][p] = *(const u16x8*)(gA[s] + int64_t(r) * lda + k0 + ch * 8);
-        rb[s][p] = *(const u16x8*)(gB[s] + int64_t(r) * ldb + k0 + ch * 8);
+      for (int p = 0; p < LP; ++p) {
+        const int c = (p * NW + wv) * 64 + lane, r = c / CPR;
+        const int ch = (c % CPR) ^ chunk_swz<CPR>(r);
+        dma16(gsrc[s] + int64_t(r) * ld + k0 + ch * 8, &lds[st][s][(p * NW + wv) * 64]);
       }
     }
   };
-  auto sstore = [&](int st) {
+  bf16x8 fa[2][NA][G::FM], fb[2][NA][G::FN];
+  auto lread = [&](int st, int ks, int buf) {
+    const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int q = t + 256 * p, r = q >> 3, ch = q & 7;
+    for (int s = 0; s < NA; ++s) {
 #pragma unroll
-      for (int s = 0; s < NA; ++s) {
-        lds[st][s][swz(r, ch)] = ra[s][p];
-        lds[st][NA + s][swz(r, ch)] = rb[s][p];
+      for (int x = 0; x < G::FM; ++x) {
+        const int r = wr + x * 32 + (lane & 31);
+        fa[buf][s][x] = as_bf16x8(lds[st][s][r * CPR + (ch ^ chunk_swz<CPR>(r))]);
+      }
+#pragma unroll
+      for (int x = 0; x < G::FN; ++x) {
+        const int r = wc + x * 32 + (lane & 31);
+        fb[buf][s][x] = as_bf16x8(lds[st][NA + s][r * CPR + (ch ^ chunk_swz<CPR>(r))]);
       }
     }
   };
-
-  const int KT = int(K / GB_K);
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < KT) gload(int64_t(kt + 1) * GB_K);
+  auto compute = [&](int st) {
+    lread(st, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = ks * 2 + (lane >> 5);
-      bf16x8 fa[NA][2], fb[NA][2];
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) lread(st, ks + 1, (ks + 1) & 1);
+      const int q = ks & 1;
 #pragma unroll
-      for (int s = 0; s < NA; ++s)
+      for (int a = 0; a < G::FM; ++a)
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          fa[s][x] = as_bf16x8(lds[st][s][swz(wr + x * 32 + (lane & 31), ch)]);
-          fb[s][x] = as_bf16x8(lds[st][NA + s][swz(wc + x * 32 + (lane & 31), ch)]);
-        }
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          acc[a][b] = mfma32x32x16(fa[0][a], fb[0][b], acc[a][b]);
-          if (NPROD == 3) {
-            acc[a][b] = mfma32x32x16(fa[0][a], fb[NA - 1][b], acc[a][b]);
-            acc[a][b] = mfma32x32x16(fa[NA - 1][a], fb[0][b], acc[a][b]);
+        for (int b = 0; b < G::FN; ++b) {
+          acc[a][b] = mfma32x32x16(fa[q][0][a], fb[q][0][b], acc[a][b]);
+          if constexpr (NPROD == 3) {
+            acc[a][b] = mfma32x32x16(fa[q][0][a], fb[q][NA - 1][b], acc[a][b]);
+            acc[a][b] = mfma32x32x16(fa[q][NA - 1][a], fb[q][0][b], acc[a][b]);
           }
         }
     }
-    if (kt + 1 < KT) sstore(st ^ 1);
-    __syncthreads();
+  };
+
+  // two stages: the loads of k-tile k+1 fly while k-tile k is multiplied;
+  // stage u^1 was last read before the barrier that ended the previous tile
+  const int KT = int(K / BK);
+  gload(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int kt = 0; kt < KT; kt += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k = kt + u;
+      if (k < KT) {
+        if (k + 1 < KT) gload(int64_t(k + 1) * BK, u ^ 1);
+        compute(u);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
+    }
   }
 
   const bool diag = upper && (ti == tj);
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < G::FM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < G::FN; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int64_t i0 = row0 + wr + a * 32 + g * 8 + (lane >> 5) * 4;
@@ -463,6 +511,45 @@ __global__ __launch_bounds__(256) void ns0_kernel(MatTable tab, StepScalars sc, 
 // ============================================================================
 static hipError_t last_launch() { return hipGetLastError(); }
 
+// One NS step of the bf16 path: Gram, poly, apply.
+template <int TILE, typename PT>
+static hipError_t ns_step_bf16(const LargeArgs& g, hipStream_t st, int k, int cur, int last) {
+  using Geo = GemmGeom<TILE>;
+  const LargeLayout& L = g.L;
+  uint8_t* ws = (uint8_t*)g.ws;
+  uint16_t* X = (uint16_t*)(ws + L.x);
+  uint16_t* Xt[2] = {(uint16_t*)(ws + L.xt0), (uint16_t*)(ws + L.xt1)};
+  float* A = (float*)(ws + L.a);
+  float* scal = (float*)(ws + L.scal);
+  uint16_t* H = (uint16_t*)(ws + L.h);
+  uint16_t* Lo = (uint16_t*)(ws + L.l);
+  uint16_t* Poff = (uint16_t*)(ws + L.poff);
+  float* Pd = (float*)(ws + L.pdiag);
+  const int64_t mp = g.mp, np = g.np;
+  if (mp % TILE != 0 || np % TILE != 0) return hipErrorInvalidValue;
+  const int Tm = int(mp / TILE), Tn = int(np / TILE);
+  const unsigned up = unsigned(Tm * (Tm + 1) / 2);
+  const dim3 blk(Geo::NT);
+  // Gram: upper tiles of [mp x mp], K = np
+  EpiGramBf16 eg{A, H, Lo, scal, k == 0, mp};
+  hipLaunchKernelGGL((gemm_bf16_kernel<TILE, 1, EpiGramBf16>), dim3(up, g.count), blk, 0, st,
+                     (const uint16_t*)X, (const uint16_t*)nullptr, np, L.x_stride, (const uint16_t*)X,
+                     (const uint16_t*)nullptr, np, L.x_stride, np, Tm, 1, eg);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  // Poly: S = HH + HL + LH over upper tiles, K = mp
+  EpiPolyBf16 ep{A, Poff, Pd, scal, k == 0, g.sc.a, g.sc.b, g.sc.c, mp, g.m};
+  hipLaunchKernelGGL((gemm_bf16_kernel<TILE, 3, EpiPolyBf16>), dim3(up, g.count), blk, 0, st,
+                     (const uint16_t*)H, (const uint16_t*)Lo, mp, L.a_stride, (const uint16_t*)H,
+                     (const uint16_t*)Lo, mp, L.a_stride, mp, Tm, 1, ep);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  // Apply: X' = Poff Xt^T + diag(Pd) X, K = mp
+  EpiApplyBf16<PT> ea{g.tab, g.sc, X, Xt[cur ^ 1], Pd, mp, np, g.m, g.n, last};
+  hipLaunchKernelGGL((gemm_bf16_kernel<TILE, 1, EpiApplyBf16<PT>>), dim3(unsigned(Tm * Tn), g.count), blk, 0,
+                     st, (const uint16_t*)Poff, (const uint16_t*)nullptr, mp, L.a_stride,
+                     (const uint16_t*)Xt[cur], (const uint16_t*)nullptr, mp, L.x_stride, mp, Tn, 0, ea);
+  return hipGetLastError();
+}
+
 template <typename PT, typename XT>
 static hipError_t run_large_t(const LargeArgs& g, hipStream_t st) {
   const LargeLayout& L = g.L;
@@ -496,29 +583,9 @@ static hipError_t run_large_t(const LargeArgs& g, hipStream_t st) {
   for (int k = 0; k < steps; ++k) {
     const int last = (k == steps - 1);
     if constexpr (sizeof(XT) == 2) {
-      uint16_t* H = (uint16_t*)(ws + L.h);
-      uint16_t* Lo = (uint16_t*)(ws + L.l);
-      uint16_t* Poff = (uint16_t*)(ws + L.poff);
-      float* Pd = (float*)(ws + L.pdiag);
-      const int Tm = int(mp / GB_M), Tn = int(np / GB_N);
-      // Gram: upper tiles of [mp x mp], K = np
-      EpiGramBf16 eg{A, H, Lo, scal, k == 0, mp};
-      hipLaunchKernelGGL((gemm_bf16_kernel<1, EpiGramBf16>), dim3(unsigned(Tm * (Tm + 1) / 2), count),
-                         dim3(256), 0, st, (const uint16_t*)X, (const uint16_t*)nullptr, np, L.x_stride,
-                         (const uint16_t*)X, (const uint16_t*)nullptr, np, L.x_stride, np, Tm, 1, eg);
-      if (hipError_t e = last_launch(); e != hipSuccess) return e;
-      // Poly: S = HH + HL + LH over upper tiles, K = mp
-      EpiPolyBf16 ep{A, Poff, Pd, scal, k == 0, g.sc.a, g.sc.b, g.sc.c, mp, m};
-      hipLaunchKernelGGL((gemm_bf16_kernel<3, EpiPolyBf16>), dim3(unsigned(Tm * (Tm + 1) / 2), count),
-                         dim3(256), 0, st, (const uint16_t*)H, (const uint16_t*)Lo, mp, L.a_stride,
-                         (const uint16_t*)H, (const uint16_t*)Lo, mp, L.a_stride, mp, Tm, 1, ep);
-      if (hipError_t e = last_launch(); e != hipSuccess) return e;
-      // Apply: X' = Poff Xt^T + diag(Pd) X, K = mp
-      EpiApplyBf16<PT> ea{g.tab, g.sc, (uint16_t*)X, (uint16_t*)Xt[cur ^ 1], Pd, mp, np, m, n, last};
-      hipLaunchKernelGGL((gemm_bf16_kernel<1, EpiApplyBf16<PT>>), dim3(unsigned(Tm * Tn), count),
-                         dim3(256), 0, st, (const uint16_t*)Poff, (const uint16_t*)nullptr, mp, L.a_stride,
-                         (const uint16_t*)Xt[cur], (const uint16_t*)nullptr, mp, L.x_stride, mp, Tn, 0, ea);
-      if (hipError_t e = last_launch(); e != hipSuccess) return e;
+      const hipError_t e = (g.tile == 256) ? ns_step_bf16<256, PT>(g, st, k, cur, last)
+                                           : ns_step_bf16<128, PT>(g, st, k, cur, last);
+      if (e != hipSuccess) return e;
     } else {
       float* Pf = (float*)(ws + L.poff);
       const int Tm = int(mp / GF_M), Tn = int(np / GF_M);

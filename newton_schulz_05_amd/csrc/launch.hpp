@@ -16,6 +16,7 @@ struct LargeArgs {
   void* ws;          // base of the chunk region in the workspace
   int count;
   int64_t m, n, mp, np;
+  int tile;          // bf16 GEMM tile (128 or 256)
   bool bf16;
 };
 

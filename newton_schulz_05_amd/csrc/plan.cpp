@@ -59,6 +59,19 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
   return L;
 }
 
+int32_t mfma_tile(int64_t m, int64_t n, int64_t count) {
+  // The 256 tile (one 8-wave block per CU) runs the large products faster
+  // but needs enough tiles to fill 256 CUs: at least 256 blocks in the
+  // symmetric launches and 512 in the apply; and it must not pad more than
+  // 10% beyond the 128 tile (m^2 n work).
+  const int64_t t = ceil_div(m, kMfmaTileBig), u = ceil_div(n, kMfmaTileBig);
+  const int64_t sym = count * t * (t + 1) / 2, full = count * t * u;
+  const double big = double(t * kMfmaTileBig) * double(t * kMfmaTileBig) * double(u * kMfmaTileBig);
+  const double small = double(round_up(m, kMfmaTile)) * double(round_up(m, kMfmaTile)) *
+                       double(round_up(n, kMfmaTile));
+  return (sym >= 256 && full >= 512 && big <= 1.10 * small) ? int32_t(kMfmaTileBig) : int32_t(kMfmaTile);
+}
+
 size_t skinny_bytes(const Group& g, int32_t count) {
   return size_t(count) * 2 * size_t(g.slabs) * size_t(kSkinnyPartStride) * 4;
 }
@@ -131,7 +144,8 @@ muon_status build_plan(const muon_shape* shapes, int32_t n_params, muon_dtype pa
       int32_t cap = (int32_t)std::min<int64_t>(kMaxChunkMats, kSkinnyCapacity / g.slabs);
       g.chunks = split_even(count, cap);
     } else {
-      const int64_t t = (g.path == PATH_MFMA) ? kMfmaTile : kF32Tile;
+      g.tile = (g.path == PATH_MFMA) ? mfma_tile(g.m, g.n, count) : int32_t(kF32Tile);
+      const int64_t t = g.tile;
       g.mp = round_up(g.m, t);
       g.np = round_up(g.n, t);
       LargeLayout one = large_layout(g, 1, param_dt);

@@ -31,7 +31,8 @@ constexpr int64_t kSkinnyWaves = 4;
 constexpr int64_t kSkinnyMaxSlab = 32 * kSkinnyBlocksPerWave * kSkinnyWaves;  // 1024 columns
 constexpr int64_t kSkinnyCapacity = 768;     // co-resident workgroups assumed (3 per CU x 256 CUs)
 constexpr int64_t kSkinnyPartStride = 1024 + 64;  // floats per slab partial (32x32 Gram + sum of squares)
-constexpr int64_t kMfmaTile = 128;           // row/column padding of the MFMA path
+constexpr int64_t kMfmaTile = 128;           // MFMA path: default GEMM tile and padding
+constexpr int64_t kMfmaTileBig = 256;        // MFMA path: tile for groups with work for the whole chip
 constexpr int64_t kF32Tile = 64;             // row/column padding of the fp32 path
 constexpr int64_t kMomTile = 64;             // momentum kernel tile (rows and columns)
 constexpr size_t kSyncBytes = 8192;          // barrier counters (skinny path)
@@ -65,6 +66,7 @@ struct Group {
   int64_t n_tr = 0;
   std::vector<Chunk> chunks;
   int64_t mp = 0, np = 0;      // padded dims (MFMA / fp32 paths)
+  int32_t tile = 0;            // MFMA path: GEMM output tile (128 or 256)
   int32_t slabs = 0;           // skinny: column slabs per matrix
   int64_t slab_w = 0;          // skinny: columns per slab (multiple of 32)
   int32_t max_chunk = 0;       // largest chunk of this group
@@ -89,6 +91,9 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt);
 
 // Bytes of the skinny partial-sum buffer for one chunk.
 size_t skinny_bytes(const Group& g, int32_t count);
+
+// GEMM tile of an MFMA-path group of `count` matrices of wide shape [m, n].
+int32_t mfma_tile(int64_t m, int64_t n, int64_t count);
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }

@@ -115,3 +115,17 @@ def test_checkpoint_resume_bitwise():
     torch.cuda.synchronize()
     for a, b in zip(params + moms, p2 + m2):
         assert torch.equal(a, b)
+
+
+def test_gemm_tile_choice_is_bitwise_neutral():
+    """Eight [2048, 2304] matrices run with 256 x 256 GEMM tiles, one alone
+    with 128 x 128 tiles (too few tiles to fill the chip at 256); per 16-wide
+    k slice both kernels take each output's MFMA products in the same order,
+    so the results must agree bit for bit.  The last matrix is tall."""
+    shapes = [(2048, 2304)] * 7 + [(2304, 2048)]
+    params, grads = _draw(shapes, torch.bfloat16, 75)
+    pg, mg = _step(shapes, [p.clone() for p in params], grads, torch.bfloat16)
+    for i in (0, 7):
+        p1, m1 = _step([shapes[i]], [params[i].clone()], [[grads[0][i]], [grads[1][i]]], torch.bfloat16)
+        assert torch.equal(p1[0], pg[i]), f"W[{i}] differs between the 128 and 256 tile kernels"
+        assert torch.equal(m1[0], mg[i])

@@ -47,6 +47,26 @@ constexpr int kGather = 12;       // partial words each thread has in flight whi
 
 __device__ __forceinline__ int row_of(int r, int h) { return ((r >> 2) << 3) + (h << 2) + (r & 3); }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
+// (lgkmcnt 0) but not for its global memory accesses, so the momentum stores
+// and the W prefetch keep draining across it.  The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt(63) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Fixed-order sum over the 256 threads (result in every thread).
+__device__ __forceinline__ float sum_256(float v, float* lds4) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) lds4[wid] = v;
+  lds_barrier();
+  return (lds4[0] + lds4[1]) + (lds4[2] + lds4[3]);
+}
+
 // Cross-workgroup exchange.  Every workgroup publishes its slab's partial
 // Gram (upper triangle, plus the sum of squares on the first step) as 8-byte
 // words that pair each value with a tag naming the call and the NS step.
@@ -81,28 +101,59 @@ struct SkShared {
   float ss[4];
 };
 
-// C = epi(i, j, (A B)[i][j]) for 32 x 32 fp32 matrices in LDS (stride 33).
-// Wave w computes the 16 x 16 quadrant (w / 2, w % 2) of C over the whole
-// contraction with the fp32 MFMA (16x16x4, fixed k order), so every
-// workgroup computes bitwise the same C.  C may alias A or B.
-template <typename Epi>
-__device__ __forceinline__ void mm32(float (*C)[33], const float (*A)[33], const float (*B)[33], int t,
-                                     Epi epi) {
+// One 16 x 16 quadrant of A B for 32 x 32 fp32 matrices in LDS (stride 33):
+// wave w takes quadrant (w / 2, w % 2) over the whole contraction with the
+// fp32 MFMA (16x16x4), even and odd k-steps in two chains added at the end.
+// The order is fixed, so every workgroup computes bitwise the same product.
+// Lane (l16, l4) ends with rows r0 + 4 l4 + r, column c0 + l16 (r = 0..3).
+// Only the first `ks` k-steps of 4 are taken: rows and columns at and beyond
+// m are zero, so ks = ceil(m / 4) loses nothing.
+__device__ __forceinline__ f32x4 quad32(const float (*A)[33], const float (*B)[33], int t, int ks) {
   const int lane = t & 63, w = t >> 6;
   const int r0 = (w >> 1) * 16, c0 = (w & 1) * 16, l16 = lane & 15, l4 = lane >> 4;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 e = f32x4{0.f, 0.f, 0.f, 0.f}, o = e;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int k = 4 * s + l4;
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r0 + l16][k], B[k][c0 + l16], acc, 0, 0, 0);
+  for (int s = 0; s < 8; s += 2) {
+    if (s < ks)
+      e = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r0 + l16][4 * s + l4], B[4 * s + l4][c0 + l16], e, 0, 0, 0);
+    if (s + 1 < ks)
+      o = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r0 + l16][4 * s + 4 + l4], B[4 * s + 4 + l4][c0 + l16], o, 0,
+                                               0, 0);
   }
-  __syncthreads();  // every operand read is done before C is overwritten
+  return e + o;
+}
+
+// C[i][j] = epi(i, j, (A B)[i][j]), then a barrier.  C must not alias A or B
+// (no barrier separates this round's reads from its writes).
+template <typename Epi>
+__device__ __forceinline__ void mm32(float (*C)[33], const float (*A)[33], const float (*B)[33], int t, int ks,
+                                     Epi epi) {
+  const f32x4 acc = quad32(A, B, t, ks);
+  const int lane = t & 63, w = t >> 6;
+  const int r0 = (w >> 1) * 16, c0 = (w & 1) * 16, l16 = lane & 15, l4 = lane >> 4;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = r0 + 4 * l4 + r, j = c0 + l16;
     C[i][j] = epi(i, j, acc[r]);
   }
-  __syncthreads();
+  lds_barrier();
+}
+
+// C1 = A1 B1 and C2 = A2 B2 in one round (the two chains overlap).
+__device__ __forceinline__ void mm32x2(float (*C1)[33], const float (*A1)[33], const float (*B1)[33],
+                                       float (*C2)[33], const float (*A2)[33], const float (*B2)[33], int t,
+                                       int ks) {
+  const f32x4 p = quad32(A1, B1, t, ks);
+  const f32x4 q = quad32(A2, B2, t, ks);
+  const int lane = t & 63, w = t >> 6;
+  const int r0 = (w >> 1) * 16, c0 = (w & 1) * 16, l16 = lane & 15, l4 = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = r0 + 4 * l4 + r, j = c0 + l16;
+    C1[i][j] = p[r];
+    C2[i][j] = q[r];
+  }
+  lds_barrier();
 }
 
 }  // namespace
@@ -266,8 +317,8 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
 #pragma unroll
     for (int r = 0; r < 16; ++r) sh.red[v][row_of(r, h) * 32 + cl] = gacc[r];
     float tot = 0.f;
-    if (with_ss) tot = block_sum_256(ss, sh.ss);  // contains __syncthreads
-    __syncthreads();
+    if (with_ss) tot = sum_256(ss, sh.ss);  // contains a barrier
+    lds_barrier();
     const uint32_t tag = (epoch << 5) | uint32_t(k + 1);
     const uint32_t dst = part_z + (uint32_t(k & 1) * S + s) * kPartW;
     for (int e = t; e < ntri; e += 256) {
@@ -291,6 +342,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
     const int t = opaque(int(threadIdx.x));
     const uint32_t tag = (epoch << 5) | uint32_t(k + 1);
     const uint32_t src = part_z + uint32_t(k & 1) * S * kPartW;
+    lds_barrier();  // every thread has read sh.red for its publish before gbuf (= sh.red) is written
     // words per slab: the triangle, plus the sum of squares on the first step
     const int nw = ntri + (first ? 1 : 0);
     // The per-wave staging area (free between publish and the last apply)
@@ -328,7 +380,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
 #pragma unroll
       for (int j = 0; j < kGather; ++j)
         if (t + 256 * j < tot) gbuf[t + 256 * j] = __uint_as_float(w[j][0]);
-      __syncthreads();
+      lds_barrier();
       // fixed slab order within and across rounds
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
@@ -336,20 +388,20 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
         if (e < nw)
           for (int q = 0; q < nq; ++q) acc[r] += gbuf[q * nw + e];
       }
-      __syncthreads();
+      lds_barrier();
     }
     float s2 = 1.f;
     if (first) {
       // word ntri (the sum of squares) is entry ntri: broadcast it via LDS
       if (t == ntri % 256) sh.ss[0] = (ntri < 256) ? acc[0] : (ntri < 512) ? acc[1] : acc[2];
-      __syncthreads();
+      lds_barrier();
       const float sn = 1.0f / (sqrtf(sh.ss[0]) + kNsEps);
       s2 = sn * sn;
       s_out = sn;
     }
     // zero the padded A, then fill both triangles
     for (int e = t; e < 32 * 33; e += 256) (&sh.A[0][0])[e] = 0.f;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
       const int e = t + 256 * r;
@@ -360,7 +412,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
         sh.A[j][i] = acc[r] * s2;
       }
     }
-    __syncthreads();
+    lds_barrier();
   };
 
   // Gram-space NS: from sh.A = A0 and s, run the recurrence and leave Q_K
@@ -377,23 +429,26 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       const int i = e / 33, j = e - i * 33;
       (&Q[0][0])[e] = (i == j && i < m) ? snorm : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     const float ca = sc.a, cb = sc.b, cc = sc.c;
     const int mm = m;
-    auto ident = [](int, int, float v) { return v; };
+    const int ks = (m + 3) >> 2;
     const int steps = sc.ns_steps;
+    // P, Q and A are polynomials in A0, so they commute: A <- P A P = P (P A).
+    // Per step: P = a I + b A + c A^2;  then Q <- P Q and T = P A together;
+    // then A <- P T (skipped after the last step).
     for (int k = 0; k < steps; ++k) {
-      // P = a I + b A + c A^2
-      mm32(P, A, A, t, [=](int i, int j, float a2) {
+      mm32(P, A, A, t, ks, [=](int i, int j, float a2) {
         float p = fmaf(cc, a2, cb * A[i][j]);
         return (i == j && i < mm) ? p + ca : p;
       });
-      mm32(Qn, P, Q, t, ident);  // Q <- P Q
-      { float (*tq)[33] = Q; Q = Qn; Qn = tq; }
       if (k + 1 < steps) {
-        mm32(T, P, A, t, ident);  // A <- P A P
-        mm32(A, T, P, t, ident);
+        mm32x2(Qn, P, Q, T, P, A, t, ks);
+        mm32(A, P, T, t, ks, [](int, int, float v) { return v; });
+      } else {
+        mm32(Qn, P, Q, t, ks, [](int, int, float v) { return v; });
       }
+      { float (*tq)[33] = Q; Q = Qn; Qn = tq; }
     }
     // Q (fp32) -> hi/lo bf16 operand registers: Q[i][kr] is k-slot q of lane
     // (h, i) in k-step tt, where X0 row kr sits at k-slot q of lane half h
@@ -405,7 +460,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       sh.pop[tt][0][hh * 32 + i][q] = hi;
       sh.pop[tt][1][hh * 32 + i][q] = f2bf(qv - bf2f(hi));
     }
-    __syncthreads();
+    lds_barrier();
   };
 
   auto apply = [&](const uint32_t* x, int lane) {
@@ -421,7 +476,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
 
   // O for one block (16 values per lane) -> fp32 store or weight update
   const float keep = 1.0f - sc.lr * sc.wd, stepc = -sc.lr * sc.scale;
-  auto emit_block = [&](const f32x16& o, int q) {
+  auto emit_block = [&](const f32x16& o, int q, const u32x4* wq) {
     const int lane = opaque(int(threadIdx.x)) & 63, h = lane >> 5, cl = lane & 31;
     if (full(q)) {
       // O through LDS (fp32, column-major, stride 33) to row-major vectors
@@ -441,7 +496,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
           buf_st_b128(rW, e0 * 4 + 16 * i, u32x4{__float_as_uint(ov[4 * i]), __float_as_uint(ov[4 * i + 1]),
                                                  __float_as_uint(ov[4 * i + 2]), __float_as_uint(ov[4 * i + 3])});
       } else {
-        const u32x4 wa = buf_ld_b128(rW, e0 * 2), wb = buf_ld_b128(rW, e0 * 2 + 16);
+        const u32x4 wa = wq[0], wb = wq[1];
         u32x4 na, nb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -481,13 +536,27 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   publish(gacc, 0, true);
   float snorm = 1.f;
   gather_a(0, true, snorm);
+  // W of the full vector blocks is read into registers now: the loads fly
+  // while the Gram-space recurrence (which touches no memory) runs.
+  u32x4 wreg[kNB][2];
+  if (step_mode) {
+    const int lane = opaque(int(threadIdx.x)) & 63;
+#pragma unroll
+    for (int q = 0; q < kNB; ++q) {
+      if (full(q)) {
+        const uint32_t e0 = row_off(q, lane);
+        wreg[q][0] = buf_ld_b128(rW, e0 * 2);
+        wreg[q][1] = buf_ld_b128(rW, e0 * 2 + 16);
+      }
+    }
+  }
   gram_space_ns(snorm);
   {
     const int lane = opaque(int(threadIdx.x)) & 63;
 #pragma unroll
     for (int q = 0; q < kNB; ++q) {
       const f32x16 acc = apply(xw[q], lane);
-      emit_block(acc, q);
+      emit_block(acc, q, wreg[q]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }

@@ -28,6 +28,48 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 
 
+# HBM traffic of the skinny kernel on the 74 x [24, 10240] workload, from two
+# rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean
+# over the profiled dispatches), each scaled by the ratio of known bytes to
+# the same counter on a plain device copy (`bench.py --copy-probe`).  Valid
+# only for the kernel source it was taken on (SHA-256 of k_skinny.hip);
+# otherwise `traffic` is reported as null.
+SKINNY_TRAFFIC = {
+    "kernel_source_sha256": "92d03779da15bf99ac2393aadd3de3b12107475208bbe7ea8c70ec47fd75f549",
+    "fetch_kib_per_dispatch": 83429.6,
+    "write_kib_per_dispatch": 113018.6,
+    "fetch_scale": 2.0,      # 262144 KiB copied / 131085.5 KiB counted
+    "write_scale": 1.0,      # 262144 KiB copied / 262144.0 KiB counted
+}
+
+
+def _kernel_sha(name: str) -> str:
+    import hashlib
+    path = os.path.join(ROOT, "newton_schulz_05_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def skinny_traffic_bytes():
+    t = SKINNY_TRAFFIC
+    if t["kernel_source_sha256"] is None or t["kernel_source_sha256"] != _kernel_sha("k_skinny.hip"):
+        return None
+    return 1024.0 * (t["fetch_kib_per_dispatch"] * t["fetch_scale"] + t["write_kib_per_dispatch"] * t["write_scale"])
+
+
+def copy_probe(nbytes: int, steps: int) -> int:
+    """A plain device copy of known size, the calibration run for the HBM
+    byte counters: each launch reads and writes `nbytes`."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": steps}), flush=True)
+    return 0
+
+
 def alg_flops(wl) -> float:
     """3 m^2 n + m^3 per matrix per NS iteration (Gram exploits symmetry)."""
     tot = 0.0
@@ -91,11 +133,16 @@ def main() -> int:
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
               "multi-GPU path: every GPU would run its own shard's step independently)", file=sys.stderr)
         return 2
+
+    if args.copy_probe:
+        return copy_probe(args.copy_probe, args.steps or 5)
 
     import torch
 
@@ -144,8 +191,9 @@ def main() -> int:
     if skinny_only:
         # one persistent kernel per chunk; with one chunk the step is one launch
         gbs = byt / (ms * 1e-3) / 1e9
+        tr = skinny_traffic_bytes() if args.config == "c2" else None
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None if tr is None else round(tr),
                 "kernel": "skinny_kernel", "launches_per_step": sum(g["n_chunks"] for g in groups)}
     elif wl.dtype == torch.bfloat16:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -70,6 +70,80 @@ def copy_probe(nbytes: int, steps: int) -> int:
     return 0
 
 
+def _events_time(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def bench_shard_update(steps, warmup):
+    """One rank's update of its 1/8 flat shard of each of two [8192, 28672]
+    bf16 matrices from their full fp32 O (the step after NS in the gathered
+    design): 8 B per shard element (W read and write 2 + 2, O read 4)."""
+    import torch
+    from newton_schulz_05_amd import shard_update
+    shape, ranks = (8192, 28672), 8
+    n = shape[0] * shape[1]
+    ws = [torch.randn(n // ranks, device="cuda").to(torch.bfloat16) for _ in range(2)]
+    os_ = [torch.randn(shape, device="cuda") * 0.01 for _ in range(2)]
+    st = torch.cuda.current_stream()
+
+    def fn():
+        for w, o in zip(ws, os_):
+            shard_update(w, o, 3 * (n // ranks), lr=0.02, wd=0.1, stream=st)
+    ms = _events_time(fn, steps, warmup, st)
+    byt = 2 * (n // ranks) * 8.0
+    gbs = byt / (ms * 1e-3) / 1e9
+    return {"metric": "shard update GB/s (rank 3 of 8, 2 x [8192, 28672] bf16, O fp32)", "value": round(gbs, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "shard_update_rank3_of8_2x8192x28672", "elements": 2 * (n // ranks)},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "shard_update_kernel",
+                         "launches_per_step": 2}}
+
+
+def bench_adamw(steps, warmup, elems):
+    """AdamW on the 1-D parameters: by default the 65 RMSNorm gains [4096] of
+    the 32-layer transformer set (launch-bound); with --adamw-elems N, 64
+    tensors of N/64 elements.  22 B per element (p 2 + 2, g 2, m 4 + 4,
+    v 4 + 4, bf16 params)."""
+    import torch
+    from newton_schulz_05_amd import AdamWGroup
+    sizes = [4096] * 65 if not elems else [elems // 64] * 64
+    ps = [torch.randn(n, device="cuda").to(torch.bfloat16) for n in sizes]
+    gs = [(torch.randn(n, device="cuda") * 1e-3).to(torch.bfloat16) for n in sizes]
+    ms = [torch.zeros(n, device="cuda") for n in sizes]
+    vs = [torch.zeros(n, device="cuda") for n in sizes]
+    st = torch.cuda.current_stream()
+    t = [0]
+
+    group = AdamWGroup(ps, gs, ms, vs)
+
+    def fn():
+        t[0] += 1
+        group.step(lr=1e-3, betas=(0.9, 0.95), eps=1e-8, wd=0.1, step=t[0], stream=st)
+    ms_ = _events_time(fn, steps, warmup, st)
+    tot = sum(sizes)
+    gbs = tot * 22.0 / (ms_ * 1e-3) / 1e9
+    name = "adamw_1d_gains_32_layers_65x4096" if not elems else f"adamw_1d_64x{elems // 64}"
+    return {"metric": "AdamW step on 1-D params (ms, GB/s)", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": round(ms_, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": name, "tensors": len(sizes), "elements": tot},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "adamw_kernel",
+                         "launches_per_step": (len(sizes) + 31) // 32}}
+
+
 def alg_flops(wl) -> float:
     """3 m^2 n + m^3 per matrix per NS iteration (Gram exploits symmetry)."""
     tot = 0.0
@@ -133,6 +207,10 @@ def main() -> int:
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="step", choices=["step", "shard_update", "adamw"],
+                    help="step: the Muon step (default); shard_update / adamw: the companion kernels")
+    ap.add_argument("--adamw-elems", type=int, default=0,
+                    help="adamw: total elements of a 64-tensor stress set instead of the model's gains")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -143,6 +221,12 @@ def main() -> int:
 
     if args.copy_probe:
         return copy_probe(args.copy_probe, args.steps or 5)
+    if args.op == "shard_update":
+        print(json.dumps(bench_shard_update(args.steps or 50, args.warmup or 5)), flush=True)
+        return 0
+    if args.op == "adamw":
+        print(json.dumps(bench_adamw(args.steps or 100, args.warmup or 10, args.adamw_elems)), flush=True)
+        return 0
 
     import torch
 

@@ -130,6 +130,73 @@ muon_status muon_ns(muon_plan plan, const void* const* in_ptrs, float* const* ou
                     const muon_shape* shapes, int32_t n_params, float a, float b, float c,
                     int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Work split over ranks --------------------------------------------
+ * Items 1(3) and 4 of the HyperParallel FSDP Muon optimizer RFC remove the
+ * redundant NS work of data-parallel ranks: each rank orthogonalises only
+ * the whole matrices assigned to it, and a greedy rule balances the load. */
+
+/* Number of matrices of the plan: a 2-D parameter counts 1, an expert slab
+ * [E, M, N] counts E.  Matrices are numbered in parameter order, the slices
+ * of a slab in order. */
+muon_status muon_plan_num_matrices(muon_plan plan, int64_t* n);
+
+/* Whole-matrix assignment of the plan's matrices to n_ranks ranks.
+ * Cost of a matrix: 3 m^2 n + m^3 with m = min and n = max of its two
+ * dimensions (the algorithmic work of one NS step).  Matrices are taken in
+ * decreasing cost, equal costs in plan order; each goes to the rank with the
+ * smallest total so far, equal totals to the lowest rank.
+ *   n_ranks   : >= 1.
+ *   owner     : host array of n_owner entries, n_owner equal to
+ *               muon_plan_num_matrices(); receives each matrix's rank.
+ *   rank_cost : NULL, or a host array of n_ranks doubles that receives each
+ *               rank's total cost.
+ * Host only and deterministic, so every rank computes the same split.  On
+ * error nothing is written. */
+muon_status muon_plan_assign(muon_plan plan, int32_t n_ranks, int32_t* owner, int64_t n_owner,
+                             double* rank_cost);
+
+/* ---- One rank's shard of a sharded parameter ------------------------------
+ * Item 1(1) of the RFC: after NS of the gathered momentum, each rank updates
+ * the slice of the parameter at its own offset. */
+
+/* W[i] <- W[i] * (1 - lr*wd) - lr*scale*O[offset + i] for 0 <= i < len, in
+ * fp32, rounded once (to nearest even) to dt.
+ *   w_shard : device, len elements of dt (MUON_BF16 or MUON_F32), in place.
+ *   o_full  : device, fp32: the whole parameter's O in its own row-major
+ *             layout, as muon_ns writes it; elements offset .. offset+len-1
+ *             are read.
+ *   offset, len : >= 0; len = 0 enqueues nothing.
+ *   lr, wd, scale : finite.
+ * Asynchronous on stream; no workspace; w_shard and o_full must not
+ * overlap. */
+muon_status muon_shard_update(void* w_shard, muon_dtype dt, const float* o_full, int64_t offset,
+                              int64_t len, float lr, float wd, float scale, void* stream);
+
+/* ---- Companion step for the 1-D parameters -------------------------------
+ * The Muon sharding optimizer of PaddlePaddle/Paddle pull request 79428
+ * ("Support Muon sharding optimizer comm overlap") keeps 2-D and 1-D
+ * parameters in separate buffers; the 1-D ones (norm gains, biases) do not
+ * go through NS and take AdamW with decoupled weight decay instead.  One call
+ * updates a whole list of them. */
+
+/* AdamW at step t >= 1 on n tensors, in fp32 per element:
+ *   p <- p (1 - lr wd)
+ *   m <- b1 m + (1 - b1) g;   v <- b2 v + (1 - b2) g^2
+ *   p <- p - (lr / (1 - b1^t)) m / (sqrt(v) / sqrt(1 - b2^t) + eps)
+ * with p rounded once to dt.
+ *   params, grads   : host arrays of n device pointers, dtype dt
+ *                     (MUON_BF16 or MUON_F32); params in place.
+ *   exp_avg, exp_avg_sq : host arrays of n device pointers, fp32, in place.
+ *   numels          : host array of n element counts (>= 0).
+ *   lr, b1, b2, eps, wd : finite; 0 <= b1, b2 < 1; eps > 0.
+ *   step            : t >= 1.
+ * Pointers must be 4-byte aligned; tensors must not overlap.  Asynchronous
+ * on stream; no workspace.  Validation happens before anything is enqueued. */
+muon_status muon_adamw_step(void* const* params, const void* const* grads, float* const* exp_avg,
+                            float* const* exp_avg_sq, const int64_t* numels, int32_t n, muon_dtype dt,
+                            float lr, float b1, float b2, float eps, float wd, int64_t step,
+                            void* stream);
+
 const char* muon_status_str(muon_status s);
 const char* muon_last_error_detail(void);
 

@@ -32,6 +32,7 @@ STATUS = {
 
 EXPORTS = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes",
            "muon_plan_num_groups", "muon_plan_group_info", "muon_step", "muon_ns",
+           "muon_plan_num_matrices", "muon_plan_assign", "muon_shard_update", "muon_adamw_step",
            "muon_status_str", "muon_last_error_detail", "muon_version"]
 
 
@@ -80,6 +81,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_step.restype = i32
     lib.muon_ns.argtypes = [vp, P(vp), P(vp), P(MuonShape), i32, f32, f32, f32, i32, vp, sz, vp]
     lib.muon_ns.restype = i32
+    lib.muon_plan_num_matrices.argtypes = [vp, P(i64)]
+    lib.muon_plan_num_matrices.restype = i32
+    lib.muon_plan_assign.argtypes = [vp, i32, P(i32), i64, P(ctypes.c_double)]
+    lib.muon_plan_assign.restype = i32
+    lib.muon_shard_update.argtypes = [vp, i32, vp, i64, i64, f32, f32, f32, vp]
+    lib.muon_shard_update.restype = i32
+    lib.muon_adamw_step.argtypes = [P(vp), P(vp), P(vp), P(vp), P(i64), i32, i32, f32, f32, f32, f32, f32, i64, vp]
+    lib.muon_adamw_step.restype = i32
     lib.muon_status_str.argtypes = [i32]
     lib.muon_status_str.restype = ctypes.c_char_p
     lib.muon_last_error_detail.argtypes = []
@@ -162,6 +171,28 @@ class MuonPlan:
             out.append(dict(m=v[0].value, n=v[1].value, count=v[2].value,
                             n_transposed=v[3].value, n_chunks=v[4].value))
         return out
+
+    def num_matrices(self) -> int:
+        """Matrices of the plan: 1 per 2-D parameter, E per expert slab."""
+        n = ctypes.c_int64()
+        _check(load_library().muon_plan_num_matrices(self._h, ctypes.byref(n)))
+        return int(n.value)
+
+    def matrices(self) -> List[Tuple[int, int]]:
+        """(parameter index, slice index) of every matrix, in plan order."""
+        out = []
+        for i, (b, _, _) in enumerate(self.shapes):
+            out.extend((i, e) for e in range(b))
+        return out
+
+    def assign(self, n_ranks: int) -> Tuple[List[int], List[float]]:
+        """Greedy whole-matrix split over n_ranks (muon_plan_assign): the
+        owner rank of every matrix and each rank's total NS cost."""
+        nm = self.num_matrices()
+        owner = (ctypes.c_int32 * max(nm, 1))()
+        cost = (ctypes.c_double * max(int(n_ranks), 1))()
+        _check(load_library().muon_plan_assign(self._h, int(n_ranks), owner, nm, cost))
+        return [int(owner[j]) for j in range(nm)], [float(cost[r]) for r in range(int(n_ranks))]
 
     def new_workspace(self, device="cuda") -> torch.Tensor:
         """Zero-filled workspace of the plan's size (a torch uint8 tensor)."""
@@ -251,3 +282,64 @@ class BoundStep:
                                    len(self.plan.shapes), lr, mu, 1 if nesterov else 0, wd, a, b, c,
                                    ns_steps, scale, self._ws, self._ws_bytes,
                                    ctypes.c_void_p(MuonPlan._stream(stream))))
+
+
+def shard_update(w_shard: torch.Tensor, o_full: torch.Tensor, offset: int, *, lr: float, wd: float = 0.0,
+                 scale: float = 1.0, stream=None) -> None:
+    """One rank's flat shard of a parameter takes the decoupled update from
+    the full O (muon_shard_update): w_shard = W.flatten()[offset:offset+len]."""
+    lib = load_library()
+    if not (w_shard.is_cuda and o_full.is_cuda):
+        raise MuonError(1, "w_shard and o_full must be device tensors")
+    if not (w_shard.is_contiguous() and o_full.is_contiguous()):
+        raise MuonError(1, "w_shard and o_full must be contiguous")
+    if o_full.dtype != torch.float32:
+        raise MuonError(3, "o_full must be float32")
+    if offset < 0 or offset + w_shard.numel() > o_full.numel():
+        raise MuonError(1, f"shard [{offset}, {offset + w_shard.numel()}) is outside O of {o_full.numel()} elements")
+    _check(lib.muon_shard_update(ctypes.c_void_p(w_shard.data_ptr()), _dtype_code(w_shard.dtype),
+                                 ctypes.c_void_p(o_full.data_ptr()), int(offset), w_shard.numel(), float(lr),
+                                 float(wd), float(scale), ctypes.c_void_p(MuonPlan._stream(stream))))
+
+
+class AdamWGroup:
+    """A fixed list of 1-D parameters with their gradients and fp32 moment
+    buffers for muon_adamw_step.  The tensors are validated once and their
+    pointer arrays kept, so each step() is one C call; their storage must not
+    be reallocated while the group is in use."""
+
+    def __init__(self, params, grads, exp_avgs, exp_avg_sqs):
+        n = len(params)
+        if not (len(grads) == len(exp_avgs) == len(exp_avg_sqs) == n):
+            raise MuonError(1, "params, grads, exp_avgs and exp_avg_sqs must have the same length")
+        self.dtype = params[0].dtype if n else torch.float32
+        for i in range(n):
+            p, g, m, v = params[i], grads[i], exp_avgs[i], exp_avg_sqs[i]
+            if p.dtype != self.dtype or g.dtype != self.dtype:
+                raise MuonError(3, f"tensor {i}: params and grads must all be {self.dtype}")
+            if m.dtype != torch.float32 or v.dtype != torch.float32:
+                raise MuonError(3, f"tensor {i}: moment buffers must be float32")
+            if not (p.numel() == g.numel() == m.numel() == v.numel()):
+                raise MuonError(2, f"tensor {i}: element counts differ")
+            if not all(t.is_cuda and t.is_contiguous() for t in (p, g, m, v)):
+                raise MuonError(1, f"tensor {i}: tensors must be contiguous device tensors")
+        self.n = n
+        self._keep = (list(params), list(grads), list(exp_avgs), list(exp_avg_sqs))
+        self._p, self._g, self._m, self._v = _ptrs(params), _ptrs(grads), _ptrs(exp_avgs), _ptrs(exp_avg_sqs)
+        self._numels = (ctypes.c_int64 * max(n, 1))(*[t.numel() for t in params])
+        self._dt = _dtype_code(self.dtype)
+        self._lib = load_library()
+
+    def step(self, *, lr: float, betas=(0.9, 0.999), eps: float = 1e-8, wd: float = 0.0, step: int,
+             stream=None) -> None:
+        b1, b2 = betas
+        _check(self._lib.muon_adamw_step(self._p, self._g, self._m, self._v, self._numels, self.n, self._dt,
+                                         lr, b1, b2, eps, wd, step, ctypes.c_void_p(MuonPlan._stream(stream))))
+
+
+def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr: float, betas=(0.9, 0.999), eps: float = 1e-8,
+               wd: float = 0.0, step: int, stream=None) -> None:
+    """AdamW on a list of 1-D parameters in one call (muon_adamw_step).
+    params/grads share a dtype (bf16 or fp32); the moment buffers are fp32."""
+    AdamWGroup(params, grads, exp_avgs, exp_avg_sqs).step(lr=lr, betas=betas, eps=eps, wd=wd, step=step,
+                                                          stream=stream)

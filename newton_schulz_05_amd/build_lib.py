@@ -23,7 +23,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-Wno-unused-variable"] + DEVICE_FLAGS
 
-SOURCES = ["plan.cpp", "api.cpp", "k_large.hip", "k_skinny.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "k_large.hip", "k_skinny.hip", "k_elem.hip"]
 
 
 def _compile(src: str) -> str:

@@ -214,6 +214,108 @@ muon_status muon_plan_group_info(muon_plan plan, int32_t g, int64_t* m, int64_t*
   return MUON_OK;
 }
 
+muon_status muon_plan_num_matrices(muon_plan plan, int64_t* n) {
+  if (!plan || !n) return fail(MUON_ERR_INVALID_ARG, "null plan or output pointer");
+  *n = (int64_t)plan->p.mats.size();
+  return MUON_OK;
+}
+
+muon_status muon_plan_assign(muon_plan plan, int32_t n_ranks, int32_t* owner, int64_t n_owner,
+                             double* rank_cost) {
+  if (!plan || !owner) return fail(MUON_ERR_INVALID_ARG, "null plan or owner array");
+  if (n_ranks < 1) return fail(MUON_ERR_INVALID_ARG, "n_ranks must be >= 1");
+  if (n_owner != (int64_t)plan->p.mats.size())
+    return fail(MUON_ERR_INVALID_ARG, "n_owner must equal the plan's number of matrices (" +
+                                          std::to_string(plan->p.mats.size()) + ")");
+  std::vector<int32_t> own;
+  std::vector<double> cost;
+  muon::assign_greedy(plan->p, n_ranks, &own, &cost);
+  std::memcpy(owner, own.data(), own.size() * sizeof(int32_t));
+  if (rank_cost) std::memcpy(rank_cost, cost.data(), cost.size() * sizeof(double));
+  return MUON_OK;
+}
+
+muon_status muon_shard_update(void* w_shard, muon_dtype dt, const float* o_full, int64_t offset, int64_t len,
+                              float lr, float wd, float scale, void* stream) {
+  if (dt != MUON_F32 && dt != MUON_BF16) return fail(MUON_ERR_DTYPE, "dt must be MUON_F32 or MUON_BF16");
+  if (offset < 0 || len < 0) return fail(MUON_ERR_INVALID_ARG, "offset and len must be >= 0");
+  if (!finite(lr) || !finite(wd) || !finite(scale)) return fail(MUON_ERR_INVALID_ARG, "lr, wd and scale must be finite");
+  if (len == 0) return MUON_OK;
+  if (!w_shard || !o_full) return fail(MUON_ERR_INVALID_ARG, "null w_shard or o_full");
+  const size_t es = (dt == MUON_BF16) ? 2 : 4;
+  const char* w0 = (const char*)w_shard;
+  const char* o0 = (const char*)(o_full + offset);
+  if (w0 < o0 + size_t(len) * 4 && o0 < w0 + size_t(len) * es)
+    return fail(MUON_ERR_INVALID_ARG, "w_shard and o_full overlap");
+  hipError_t e = muon::run_shard_update(w_shard, dt == MUON_BF16, o_full + offset, len, lr, wd, scale,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return MUON_OK;
+}
+
+muon_status muon_adamw_step(void* const* params, const void* const* grads, float* const* exp_avg,
+                            float* const* exp_avg_sq, const int64_t* numels, int32_t n, muon_dtype dt,
+                            float lr, float b1, float b2, float eps, float wd, int64_t step, void* stream) {
+  if (dt != MUON_F32 && dt != MUON_BF16) return fail(MUON_ERR_DTYPE, "dt must be MUON_F32 or MUON_BF16");
+  if (n < 0) return fail(MUON_ERR_INVALID_ARG, "n must be >= 0");
+  if (n > 0 && (!params || !grads || !exp_avg || !exp_avg_sq || !numels))
+    return fail(MUON_ERR_INVALID_ARG, "null pointer array");
+  if (!finite(lr) || !finite(b1) || !finite(b2) || !finite(eps) || !finite(wd))
+    return fail(MUON_ERR_INVALID_ARG, "lr, b1, b2, eps and wd must be finite");
+  if (!(b1 >= 0.f && b1 < 1.f && b2 >= 0.f && b2 < 1.f)) return fail(MUON_ERR_INVALID_ARG, "b1 and b2 must be in [0, 1)");
+  if (!(eps > 0.f)) return fail(MUON_ERR_INVALID_ARG, "eps must be > 0");
+  if (step < 1) return fail(MUON_ERR_INVALID_ARG, "step must be >= 1");
+  for (int32_t i = 0; i < n; ++i) {
+    if (numels[i] < 0) return fail(MUON_ERR_SHAPE, "numels[" + std::to_string(i) + "] < 0");
+    if (numels[i] == 0) continue;
+    const void* ptrs[4] = {params[i], grads[i], exp_avg[i], exp_avg_sq[i]};
+    for (const void* q : ptrs)
+      if (!q) return fail(MUON_ERR_INVALID_ARG, "null tensor pointer at " + std::to_string(i));
+      else if ((uintptr_t)q % 4 != 0) return fail(MUON_ERR_ALIGNMENT, "tensor " + std::to_string(i) + " not 4-byte aligned");
+    if (numels[i] > (int64_t(1) << 40)) return fail(MUON_ERR_SHAPE, "tensor too large");
+  }
+  // step size and bias corrections in double, rounded once to fp32
+  const double t = double(step);
+  muon::AdamScalars sc;
+  sc.lr = lr; sc.b1 = b1; sc.b2 = b2; sc.eps = eps; sc.wd = wd;
+  sc.step_size = float(double(lr) / (1.0 - std::pow(double(b1), t)));
+  sc.bc2_sqrt = float(std::sqrt(1.0 - std::pow(double(b2), t)));
+  const hipStream_t st = (hipStream_t)stream;
+  muon::AdamTable tab;
+  tab.n = 0;
+  tab.first_block[0] = 0;
+  auto flush = [&]() -> hipError_t {
+    if (tab.n == 0) return hipSuccess;
+    hipError_t e = muon::run_adamw(tab, sc, dt == MUON_BF16, st);
+    tab.n = 0;
+    tab.first_block[0] = 0;
+    return e;
+  };
+  for (int32_t i = 0; i < n; ++i) {
+    if (numels[i] == 0) continue;
+    int64_t done = 0;
+    while (done < numels[i]) {  // a tensor larger than one launch's block budget is split
+      const int64_t room = (int64_t(1) << 30) - tab.first_block[tab.n];
+      if (tab.n == muon::kAdamMaxTensors || room < 1) {
+        if (hipError_t e = flush(); e != hipSuccess) return fail(MUON_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        continue;
+      }
+      const int64_t take = std::min<int64_t>(numels[i] - done, room * muon::kAdamChunk);
+      const size_t es = (dt == MUON_BF16) ? 2 : 4;
+      tab.p[tab.n] = (char*)params[i] + done * es;
+      tab.g[tab.n] = (const char*)grads[i] + done * es;
+      tab.m[tab.n] = exp_avg[i] + done;
+      tab.v[tab.n] = exp_avg_sq[i] + done;
+      tab.numel[tab.n] = take;
+      tab.first_block[tab.n + 1] = tab.first_block[tab.n] + int32_t((take + muon::kAdamChunk - 1) / muon::kAdamChunk);
+      tab.n++;
+      done += take;
+    }
+  }
+  if (hipError_t e = flush(); e != hipSuccess) return fail(MUON_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return MUON_OK;
+}
+
 muon_status muon_step(muon_plan plan, void* const* param_ptrs, const void* const* grad_ptrs,
                       void* const* mom_ptrs, const muon_shape* shapes, int32_t n_params, float lr,
                       float mu, int32_t nesterov, float wd, float a, float b, float c, int32_t ns_steps,

@@ -39,4 +39,25 @@ hipError_t run_large(const LargeArgs& a, hipStream_t st);
 hipError_t run_skinny(const SkinnyArgs& a, hipStream_t st);
 int skinny_max_blocks_per_cu();
 
+// W[i] <- W[i] (1 - lr wd) - lr scale O[i], i < len (one rank's shard of a parameter).
+hipError_t run_shard_update(void* w, bool bf16, const float* o, int64_t len, float lr, float wd, float scale,
+                            hipStream_t st);
+
+// AdamW over a list of 1-D tensors (pointer table in the kernel arguments).
+constexpr int kAdamMaxTensors = 32;       // tensors per launch
+constexpr int64_t kAdamChunk = 2048;      // elements per workgroup
+struct AdamTable {
+  void* p[kAdamMaxTensors];
+  const void* g[kAdamMaxTensors];
+  float* m[kAdamMaxTensors];
+  float* v[kAdamMaxTensors];
+  int64_t numel[kAdamMaxTensors];
+  int32_t first_block[kAdamMaxTensors + 1];  // prefix sums of ceil(numel / kAdamChunk)
+  int32_t n;
+};
+struct AdamScalars {
+  float lr, b1, b2, eps, wd, step_size, bc2_sqrt;  // step_size = lr / (1 - b1^t), bc2_sqrt = sqrt(1 - b2^t)
+};
+hipError_t run_adamw(const AdamTable& t, const AdamScalars& s, bool bf16, hipStream_t st);
+
 }  // namespace muon

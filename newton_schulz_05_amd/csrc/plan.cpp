@@ -3,6 +3,8 @@
 
 #include <algorithm>
 #include <map>
+#include <numeric>
+#include <queue>
 #include <utility>
 
 namespace muon {
@@ -57,6 +59,34 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
   L.scal = take(size_t(count) * 4 * 4);
   L.bytes = off;
   return L;
+}
+
+double ns_cost(int64_t rows, int64_t cols) {
+  const double m = double(std::min(rows, cols)), n = double(std::max(rows, cols));
+  return 3.0 * m * m * n + m * m * m;
+}
+
+void assign_greedy(const Plan& P, int32_t n_ranks, std::vector<int32_t>* owner, std::vector<double>* cost) {
+  const size_t nm = P.mats.size();
+  std::vector<double> c(nm);
+  for (size_t j = 0; j < nm; ++j) c[j] = ns_cost(P.mats[j].rows, P.mats[j].cols);
+  std::vector<size_t> order(nm);
+  std::iota(order.begin(), order.end(), size_t(0));
+  std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return c[x] > c[y]; });
+  // min-heap of (total, rank): the least loaded rank, lowest rank on ties
+  using Slot = std::pair<double, int32_t>;
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+  for (int32_t r = 0; r < n_ranks; ++r) heap.push(Slot{0.0, r});
+  owner->assign(nm, 0);
+  cost->assign(size_t(n_ranks), 0.0);
+  for (size_t j : order) {
+    Slot s = heap.top();
+    heap.pop();
+    (*owner)[j] = s.second;
+    s.first += c[j];
+    (*cost)[size_t(s.second)] = s.first;
+    heap.push(s);
+  }
 }
 
 int32_t mfma_tile(int64_t m, int64_t n, int64_t count) {

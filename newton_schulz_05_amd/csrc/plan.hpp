@@ -92,6 +92,15 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt);
 // Bytes of the skinny partial-sum buffer for one chunk.
 size_t skinny_bytes(const Group& g, int32_t count);
 
+// NS cost 3 m^2 n + m^3 of one matrix (m = min, n = max of its dimensions).
+double ns_cost(int64_t rows, int64_t cols);
+
+// Greedy whole-matrix assignment of the plan's matrices to n_ranks ranks
+// (largest cost first, each to the least loaded rank; ties in plan order and
+// to the lowest rank).  owner[j] is the rank of matrix j; cost[r] the total
+// of rank r.
+void assign_greedy(const Plan& P, int32_t n_ranks, std::vector<int32_t>* owner, std::vector<double>* cost);
+
 // GEMM tile of an MFMA-path group of `count` matrices of wide shape [m, n].
 int32_t mfma_tile(int64_t m, int64_t n, int64_t count);
 

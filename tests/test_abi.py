@@ -120,3 +120,17 @@ def test_product_path_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "muon_ref" not in text, f
+
+
+def test_shard_update_rejects_bad_calls_before_launch():
+    lib = B.load_library()
+    fake_w, fake_o = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000)
+    assert lib.muon_shard_update(fake_w, 7, fake_o, 0, 16, 0.1, 0.0, 1.0, None) == 3      # dtype
+    assert lib.muon_shard_update(fake_w, B.MUON_BF16, fake_o, -1, 16, 0.1, 0.0, 1.0, None) == 1
+    assert lib.muon_shard_update(fake_w, B.MUON_BF16, fake_o, 0, -4, 0.1, 0.0, 1.0, None) == 1
+    assert lib.muon_shard_update(fake_w, B.MUON_F32, fake_o, 0, 16, float("nan"), 0.0, 1.0, None) == 1
+    assert lib.muon_shard_update(None, B.MUON_F32, fake_o, 0, 16, 0.1, 0.0, 1.0, None) == 1
+    # overlapping W shard and O range
+    assert lib.muon_shard_update(ctypes.c_void_p(0x900010), B.MUON_F32, fake_o, 0, 64, 0.1, 0.0, 1.0, None) == 1
+    # len = 0 enqueues nothing and succeeds
+    assert lib.muon_shard_update(fake_w, B.MUON_BF16, fake_o, 5, 0, 0.1, 0.0, 1.0, None) == 0

@@ -106,29 +106,34 @@ struct SkShared {
 // fp32 MFMA (16x16x4), even and odd k-steps in two chains added at the end.
 // The order is fixed, so every workgroup computes bitwise the same product.
 // Lane (l16, l4) ends with rows r0 + 4 l4 + r, column c0 + l16 (r = 0..3).
-// Only the first `ks` k-steps of 4 are taken: rows and columns at and beyond
-// m are zero, so ks = ceil(m / 4) loses nothing.
-__device__ __forceinline__ f32x4 quad32(const float (*A)[33], const float (*B)[33], int t, int ks) {
+// Only the first KS k-steps of 4 are taken: rows and columns at and beyond
+// m are zero, so KS >= ceil(m / 4) loses nothing.  Every operand is read
+// from LDS before the first MFMA, and the products alternate between two
+// accumulators (even and odd k-steps), added at the end.
+template <int KS>
+__device__ __forceinline__ f32x4 quad32(const float (*A)[33], const float (*B)[33], int t) {
   const int lane = t & 63, w = t >> 6;
   const int r0 = (w >> 1) * 16, c0 = (w & 1) * 16, l16 = lane & 15, l4 = lane >> 4;
+  float a[KS], b[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    a[s] = A[r0 + l16][4 * s + l4];
+    b[s] = B[4 * s + l4][c0 + l16];
+  }
   f32x4 e = f32x4{0.f, 0.f, 0.f, 0.f}, o = e;
 #pragma unroll
-  for (int s = 0; s < 8; s += 2) {
-    if (s < ks)
-      e = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r0 + l16][4 * s + l4], B[4 * s + l4][c0 + l16], e, 0, 0, 0);
-    if (s + 1 < ks)
-      o = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r0 + l16][4 * s + 4 + l4], B[4 * s + 4 + l4][c0 + l16], o, 0,
-                                               0, 0);
+  for (int s = 0; s < KS; s += 2) {
+    e = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], e, 0, 0, 0);
+    if (s + 1 < KS) o = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s + 1], b[s + 1], o, 0, 0, 0);
   }
   return e + o;
 }
 
 // C[i][j] = epi(i, j, (A B)[i][j]), then a barrier.  C must not alias A or B
 // (no barrier separates this round's reads from its writes).
-template <typename Epi>
-__device__ __forceinline__ void mm32(float (*C)[33], const float (*A)[33], const float (*B)[33], int t, int ks,
-                                     Epi epi) {
-  const f32x4 acc = quad32(A, B, t, ks);
+template <int KS, typename Epi>
+__device__ __forceinline__ void mm32(float (*C)[33], const float (*A)[33], const float (*B)[33], int t, Epi epi) {
+  const f32x4 acc = quad32<KS>(A, B, t);
   const int lane = t & 63, w = t >> 6;
   const int r0 = (w >> 1) * 16, c0 = (w & 1) * 16, l16 = lane & 15, l4 = lane >> 4;
 #pragma unroll
@@ -140,11 +145,11 @@ __device__ __forceinline__ void mm32(float (*C)[33], const float (*A)[33], const
 }
 
 // C1 = A1 B1 and C2 = A2 B2 in one round (the two chains overlap).
+template <int KS>
 __device__ __forceinline__ void mm32x2(float (*C1)[33], const float (*A1)[33], const float (*B1)[33],
-                                       float (*C2)[33], const float (*A2)[33], const float (*B2)[33], int t,
-                                       int ks) {
-  const f32x4 p = quad32(A1, B1, t, ks);
-  const f32x4 q = quad32(A2, B2, t, ks);
+                                       float (*C2)[33], const float (*A2)[33], const float (*B2)[33], int t) {
+  const f32x4 p = quad32<KS>(A1, B1, t);
+  const f32x4 q = quad32<KS>(A2, B2, t);
   const int lane = t & 63, w = t >> 6;
   const int r0 = (w >> 1) * 16, c0 = (w & 1) * 16, l16 = lane & 15, l4 = lane >> 4;
 #pragma unroll
@@ -158,8 +163,10 @@ __device__ __forceinline__ void mm32x2(float (*C1)[33], const float (*A1)[33], c
 
 }  // namespace
 
-// MODE 0: muon_step (momentum in, weight update out); MODE 1: muon_ns (O out)
-template <typename PT, int MODE>
+// MODE 0: muon_step (momentum in, weight update out); MODE 1: muon_ns (O out).
+// KS: k-steps of 4 in the m x m products of the Gram-space recurrence,
+// 6 when m <= 24, else 8.
+template <typename PT, int MODE, int KS>
 __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalars sc, int m, int64_t n,
                                                         int S, int64_t slab_w, float* __restrict__ part,
                                                         uint32_t* __restrict__ sync, unsigned spin_limit,
@@ -219,6 +226,25 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
     return (r < m) ? uint32_t(r * nn + c0 + (v * kNB + q) * 32 + 16 * hc) : kOob;
   };
   u32x4 pg[2][2], pm[2][4];  // prefetched G and M of a block (ping-pong by block parity)
+  // Gram contribution of one block: stage the block column-major in this
+  // wave's LDS area, read it back row-per-lane, one MFMA per 16 columns.
+  // Taken per block inside the momentum loop, while the next block's loads
+  // are in flight.
+  auto gram_block = [&](const uint32_t* x, f32x16& gacc, int lane) {
+    const int h = lane >> 5, cl = lane & 31;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) *(u32x2*)(stg + cl * kLdr + 8 * g + 4 * h) = u32x2{x[2 * g], x[2 * g + 1]};
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      u16x8 f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = stg[(16 * tt + 8 * h + e) * kLdr + cl];
+      const bf16x8 fb = as_bf16x8(f);
+      gacc = mfma32x32x16(fb, fb, gacc);
+    }
+  };
+
+  f32x16 gacc = f32x16{};
   auto issue = [&](int q) {
     const uint32_t e0 = row_off(q, opaque(int(threadIdx.x)) & 63);
     pg[q & 1][0] = buf_ld_b128(rG, e0 * 2);
@@ -291,25 +317,10 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       for (int d = 0; d < 8; ++d) xw[q][d] = f2bf2(uu[2 * d], uu[2 * d + 1]);
     }
     __builtin_amdgcn_sched_barrier(0);
+    gram_block(xw[q], gacc, opaque(int(threadIdx.x)) & 63);
   }
 
   // ---- helpers ---------------------------------------------------------------
-  // Gram contribution of one block: stage the block column-major in this
-  // wave's LDS area, read it back row-per-lane, one MFMA per 16 columns.
-  auto gram_block = [&](const uint32_t* x, f32x16& gacc, int lane) {
-    const int h = lane >> 5, cl = lane & 31;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) *(u32x2*)(stg + cl * kLdr + 8 * g + 4 * h) = u32x2{x[2 * g], x[2 * g + 1]};
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      u16x8 f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = stg[(16 * tt + 8 * h + e) * kLdr + cl];
-      const bf16x8 fb = as_bf16x8(f);
-      gacc = mfma32x32x16(fb, fb, gacc);
-    }
-  };
-
   // combine the 4 wave partials and publish this slab's partial for NS step
   // k: upper triangle of the Gram, then (first step) the sum of squares
   auto publish = [&](const f32x16& gacc, int k, bool with_ss) {
@@ -432,21 +443,20 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
     lds_barrier();
     const float ca = sc.a, cb = sc.b, cc = sc.c;
     const int mm = m;
-    const int ks = (m + 3) >> 2;
     const int steps = sc.ns_steps;
     // P, Q and A are polynomials in A0, so they commute: A <- P A P = P (P A).
     // Per step: P = a I + b A + c A^2;  then Q <- P Q and T = P A together;
     // then A <- P T (skipped after the last step).
     for (int k = 0; k < steps; ++k) {
-      mm32(P, A, A, t, ks, [=](int i, int j, float a2) {
+      mm32<KS>(P, A, A, t, [=](int i, int j, float a2) {
         float p = fmaf(cc, a2, cb * A[i][j]);
         return (i == j && i < mm) ? p + ca : p;
       });
       if (k + 1 < steps) {
-        mm32x2(Qn, P, Q, T, P, A, t, ks);
-        mm32(A, P, T, t, ks, [](int, int, float v) { return v; });
+        mm32x2<KS>(Qn, P, Q, T, P, A, t);
+        mm32<KS>(A, P, T, t, [](int, int, float v) { return v; });
       } else {
-        mm32(Qn, P, Q, t, ks, [](int, int, float v) { return v; });
+        mm32<KS>(Qn, P, Q, t, [](int, int, float v) { return v; });
       }
       { float (*tq)[33] = Q; Q = Qn; Qn = tq; }
     }
@@ -496,7 +506,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
           buf_st_b128(rW, e0 * 4 + 16 * i, u32x4{__float_as_uint(ov[4 * i]), __float_as_uint(ov[4 * i + 1]),
                                                  __float_as_uint(ov[4 * i + 2]), __float_as_uint(ov[4 * i + 3])});
       } else {
-        const u32x4 wa = wq[0], wb = wq[1];
+        const u32x4 wa = buf_ld_b128(rW, e0 * 2), wb = buf_ld_b128(rW, e0 * 2 + 16);
         u32x4 na, nb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -527,57 +537,49 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   };
 
   // ---- Gram of X0, one exchange, Gram-space NS, apply and update ------------
-  f32x16 gacc = f32x16{};
-  {
-    const int lane = opaque(int(threadIdx.x)) & 63;
-#pragma unroll
-    for (int q = 0; q < kNB; ++q) gram_block(xw[q], gacc, lane);
-  }
   publish(gacc, 0, true);
   float snorm = 1.f;
   gather_a(0, true, snorm);
-  // W of the full vector blocks is read into registers now: the loads fly
-  // while the Gram-space recurrence (which touches no memory) runs.
-  u32x4 wreg[kNB][2];
-  if (step_mode) {
-    const int lane = opaque(int(threadIdx.x)) & 63;
-#pragma unroll
-    for (int q = 0; q < kNB; ++q) {
-      if (full(q)) {
-        const uint32_t e0 = row_off(q, lane);
-        wreg[q][0] = buf_ld_b128(rW, e0 * 2);
-        wreg[q][1] = buf_ld_b128(rW, e0 * 2 + 16);
-      }
-    }
-  }
   gram_space_ns(snorm);
   {
     const int lane = opaque(int(threadIdx.x)) & 63;
 #pragma unroll
     for (int q = 0; q < kNB; ++q) {
       const f32x16 acc = apply(xw[q], lane);
-      emit_block(acc, q, wreg[q]);
+      emit_block(acc, q, nullptr);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-hipError_t run_skinny(const SkinnyArgs& g, hipStream_t st) {
+template <int MODE, int KS>
+static void launch_skinny(const SkinnyArgs& g, hipStream_t st) {
   const unsigned grid = unsigned(g.count * g.slabs);
-  if (g.sc.mode == 0)
-    hipLaunchKernelGGL((skinny_kernel<uint16_t, 0>), dim3(grid), dim3(256), 0, st, g.tab, g.sc, g.m, g.n,
-                       g.slabs, g.slab_w, g.part, g.sync, g.spin_limit, g.epoch);
-  else
-    hipLaunchKernelGGL((skinny_kernel<uint16_t, 1>), dim3(grid), dim3(256), 0, st, g.tab, g.sc, g.m, g.n,
-                       g.slabs, g.slab_w, g.part, g.sync, g.spin_limit, g.epoch);
+  hipLaunchKernelGGL((skinny_kernel<uint16_t, MODE, KS>), dim3(grid), dim3(256), 0, st, g.tab, g.sc, g.m, g.n,
+                     g.slabs, g.slab_w, g.part, g.sync, g.spin_limit, g.epoch);
+}
+
+hipError_t run_skinny(const SkinnyArgs& g, hipStream_t st) {
+  const bool small = g.m <= 24;
+  if (g.sc.mode == 0) {
+    if (small) launch_skinny<0, 6>(g, st); else launch_skinny<0, 8>(g, st);
+  } else {
+    if (small) launch_skinny<1, 6>(g, st); else launch_skinny<1, 8>(g, st);
+  }
   return hipGetLastError();
 }
 
 int skinny_max_blocks_per_cu() {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, skinny_kernel<uint16_t, 0>, 256, 0) != hipSuccess)
-    return 0;
-  return nb;
+  // the capacity the persistent launch relies on: the least of the variants
+  int lo = 1 << 30;
+  const void* ks[4] = {(const void*)skinny_kernel<uint16_t, 0, 6>, (const void*)skinny_kernel<uint16_t, 0, 8>,
+                       (const void*)skinny_kernel<uint16_t, 1, 6>, (const void*)skinny_kernel<uint16_t, 1, 8>};
+  for (const void* k : ks) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, 256, 0) != hipSuccess) return 0;
+    lo = std::min(lo, nb);
+  }
+  return lo;
 }
 
 }  // namespace muon

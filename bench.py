@@ -35,9 +35,9 @@ F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 # only for the kernel source it was taken on (SHA-256 of k_skinny.hip);
 # otherwise `traffic` is reported as null.
 SKINNY_TRAFFIC = {
-    "kernel_source_sha256": "92d03779da15bf99ac2393aadd3de3b12107475208bbe7ea8c70ec47fd75f549",
-    "fetch_kib_per_dispatch": 83429.6,
-    "write_kib_per_dispatch": 113018.6,
+    "kernel_source_sha256": "21563d33cd868090958f3c0b994fe2d9c7a7882dd29841c718448b05ac4171d8",
+    "fetch_kib_per_dispatch": 82995.6,
+    "write_kib_per_dispatch": 109306.4,
     "fetch_scale": 2.0,      # 262144 KiB copied / 131085.5 KiB counted
     "write_scale": 1.0,      # 262144 KiB copied / 262144.0 KiB counted
 }

@@ -123,10 +123,76 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ nor
 }
 
 // ============================================================================
-// Epilogues.  The GEMM mainloops hand each a run of 4 consecutive rows
-// (i0 .. i0+3) of one column j; `diag` is true on tiles on the diagonal of a
-// symmetric output, where only i <= j is owned (and mirrored to (j, i)).
+// Epilogues.
+//
+// bf16 MFMA path: the GEMM stages each 32 x 32 MFMA tile of the output
+// through LDS and hands the epilogue
+//   row(z, i, j0, v[16], diag): C[i][j0 .. j0+15], which it may replace by
+//       the final values (the column pass sees them), and
+//   col(z, j, i0, v[16], diag): the final values C[i0 .. i0+15][j], for the
+//       mirrored (symmetric outputs) or transposed (X^T, tall W) stores,
+// so that every store is a run of 16 consecutive elements (16-byte vectors
+// where aligned).  `diag` is true on tiles on the diagonal of a symmetric
+// output, where only i <= j is owned by the row pass and i < j is mirrored.
+// fp32 path: the GEMM hands a run of 4 consecutive rows (i0 .. i0+3) of one
+// column j.
 // ============================================================================
+
+// 16 consecutive elements; elements [k0, k1) are loaded / stored (the
+// others of v are left alone), with 16-byte vectors when the run is whole
+// and aligned.
+template <typename T> struct Seg;
+template <> struct Seg<float> {
+  __device__ static __forceinline__ void load(const float* p, int k0, int k1, float* v) {
+    if (k0 == 0 && k1 == 16 && ((uintptr_t)p & 15) == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 x = ((const f32x4*)p)[q];
+        v[4 * q] = x[0]; v[4 * q + 1] = x[1]; v[4 * q + 2] = x[2]; v[4 * q + 3] = x[3];
+      }
+      return;
+    }
+    for (int k = k0; k < k1; ++k) v[k] = p[k];
+  }
+  __device__ static __forceinline__ void store(float* p, int k0, int k1, const float* v) {
+    if (k0 == 0 && k1 == 16 && ((uintptr_t)p & 15) == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ((f32x4*)p)[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+      return;
+    }
+    for (int k = k0; k < k1; ++k) p[k] = v[k];
+  }
+};
+template <> struct Seg<uint16_t> {
+  __device__ static __forceinline__ void load(const uint16_t* p, int k0, int k1, float* v) {
+    if (k0 == 0 && k1 == 16 && ((uintptr_t)p & 15) == 0) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const u32x4 x = ((const u32x4*)p)[q];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          v[8 * q + 2 * d] = bf2f(uint16_t(x[d] & 0xffffu));
+          v[8 * q + 2 * d + 1] = bf2f(uint16_t(x[d] >> 16));
+        }
+      }
+      return;
+    }
+    for (int k = k0; k < k1; ++k) v[k] = bf2f(p[k]);
+  }
+  __device__ static __forceinline__ void store(uint16_t* p, int k0, int k1, const float* v) {
+    if (k0 == 0 && k1 == 16 && ((uintptr_t)p & 15) == 0) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        ((u32x4*)p)[q] = u32x4{f2bf2(v[8 * q], v[8 * q + 1]), f2bf2(v[8 * q + 2], v[8 * q + 3]),
+                               f2bf2(v[8 * q + 4], v[8 * q + 5]), f2bf2(v[8 * q + 6], v[8 * q + 7])};
+      return;
+    }
+    for (int k = k0; k < k1; ++k) p[k] = f2bf(v[k]);
+  }
+};
+
+__device__ __forceinline__ int clamp16(int64_t x) { return x <= 0 ? 0 : (x >= 16 ? 16 : int(x)); }
+
 struct NatStore {
   // store O (fp32) or apply the weight update at the matrix's stored position
   template <typename PT>
@@ -143,79 +209,114 @@ struct NatStore {
       Elem<PT>::store(W + idx, fmaf(-sc.lr * sc.scale, o, w * keep));
     }
   }
-};
-
-// Gram (bf16 path): A = sc2 * acc, plus its bf16 hi/lo split
-struct EpiGramBf16 {
-  float* A; uint16_t* H; uint16_t* L; const float* scal; int use_scale; int64_t mp;
-  __device__ __forceinline__ void operator()(int z, int64_t i0, int64_t j, const float* v, bool diag) const {
-    const float s2 = use_scale ? scal[z * 4 + 1] : 1.0f;
-    const int64_t base = int64_t(z) * mp * mp;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t i = i0 + q;
-      if (diag && i > j) continue;
-      const float a = v[q] * s2;
-      const uint16_t h = f2bf(a);
-      const uint16_t l = f2bf(a - bf2f(h));
-      A[base + i * mp + j] = a; H[base + i * mp + j] = h; L[base + i * mp + j] = l;
-      if (i != j) { A[base + j * mp + i] = a; H[base + j * mp + i] = h; L[base + j * mp + i] = l; }
+  // the same for `cnt` consecutive stored elements starting at idx0
+  template <typename PT>
+  __device__ static __forceinline__ void put_seg(const MatRef& r, const StepScalars& sc, int64_t idx0, int cnt,
+                                                 const float* o) {
+    if (cnt <= 0) return;
+    if (sc.mode == 1) {
+      Seg<float>::store((float*)r.w + idx0, 0, cnt, o);
+      return;
     }
+    PT* W = (PT*)r.w + idx0;
+    float w[16];
+    Seg<PT>::load(W, 0, cnt, w);
+    const float keep = 1.0f - sc.lr * sc.wd;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) w[k] = fmaf(-sc.lr * sc.scale, o[k], w[k] * keep);
+    Seg<PT>::store(W, 0, cnt, w);
   }
 };
 
-// Poly (bf16 path): P = ps*(a I + b A + c S); off-diagonal bf16, diagonal fp32
+// Gram (bf16 path): A = sc2 * acc (upper tiles only: its only reader is the
+// poly epilogue at the same positions), plus its bf16 hi/lo split H, L, which
+// are GEMM operands and so are mirrored.
+struct EpiGramBf16 {
+  float* A; uint16_t* H; uint16_t* L; const float* scal; int use_scale; int64_t mp;
+  static constexpr bool kCol = true;
+  __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool diag) const {
+    const float s2 = use_scale ? scal[z * 4 + 1] : 1.0f;
+    float lo[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v[k] *= s2;
+      lo[k] = v[k] - bf2f(f2bf(v[k]));
+    }
+    const int k0 = diag ? clamp16(i - j0) : 0;  // diagonal tiles: j >= i
+    const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
+    Seg<float>::store(A + o, k0, 16, v);
+    Seg<uint16_t>::store(H + o, k0, 16, v);
+    Seg<uint16_t>::store(L + o, k0, 16, lo);
+  }
+  __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
+    float lo[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
+    const int k1 = diag ? clamp16(j - i0) : 16;  // diagonal tiles: mirror i < j only
+    const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
+    Seg<uint16_t>::store(H + o, 0, k1, v);
+    Seg<uint16_t>::store(L + o, 0, k1, lo);
+  }
+};
+
+// Poly (bf16 path): P = ps*(a I + b A + c S); off-diagonal bf16 (mirrored),
+// diagonal fp32 in Pd
 struct EpiPolyBf16 {
   const float* A; uint16_t* Poff; float* Pd; const float* scal; int use_scale;
   float a, b, c; int64_t mp, m;
-  __device__ __forceinline__ void operator()(int z, int64_t i0, int64_t j, const float* v, bool diag) const {
+  static constexpr bool kCol = true;
+  __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool diag) const {
     const float ps = use_scale ? scal[z * 4 + 0] : 1.0f;
-    const int64_t base = int64_t(z) * mp * mp;
+    const int k0 = diag ? clamp16(i - j0) : 0;
+    const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
+    float av[16] = {}, pv[16];
+    Seg<float>::load(A + o, k0, 16, av);  // positions below k0 are not used
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t i = i0 + q;
-      if (diag && i > j) continue;
-      const float av = A[base + i * mp + j];
-      float p = fmaf(c, v[q], b * av);
-      if (i == j) {
+    for (int k = 0; k < 16; ++k) {
+      float p = fmaf(c, v[k], b * av[k]);
+      if (i == j0 + k) {
         p = ps * (p + a);
-        Poff[base + i * mp + j] = 0;
         Pd[int64_t(z) * mp + i] = (i < m) ? p : 0.f;
+        pv[k] = 0.f;
       } else {
         p = ps * p;
-        const uint16_t ph = f2bf(p);
-        Poff[base + i * mp + j] = ph;
-        Poff[base + j * mp + i] = ph;
+        pv[k] = p;
       }
+      v[k] = p;
     }
+    Seg<uint16_t>::store(Poff + o, k0, 16, pv);
+  }
+  __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
+    const int k1 = diag ? clamp16(j - i0) : 16;
+    Seg<uint16_t>::store(Poff + int64_t(z) * mp * mp + j * mp + i0, 0, k1, v);
   }
 };
 
-// Apply (bf16 path): X' = acc + Pd[i] * X[i][j]
+// Apply (bf16 path): X' = acc + Pd[i] * X[i][j]; X' and X'^T in bf16, or on
+// the last step the weight update (O) at the stored position
 template <typename PT>
 struct EpiApplyBf16 {
   MatTable tab; StepScalars sc; uint16_t* X; uint16_t* XtN; const float* Pd;
   int64_t mp, np, m, n; int last;
-  __device__ __forceinline__ void operator()(int z, int64_t i0, int64_t j, const float* v, bool) const {
-    uint16_t* Xz = X + int64_t(z) * mp * np;
-    float o[4];
+  static constexpr bool kCol = true;
+  __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool) const {
+    uint16_t* Xr = X + int64_t(z) * mp * np + i * np + j0;
+    float x[16];
+    Seg<uint16_t>::load(Xr, 0, 16, x);
+    const float d = Pd[int64_t(z) * mp + i];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t i = i0 + q;
-      o[q] = fmaf(Pd[int64_t(z) * mp + i], bf2f(Xz[i * np + j]), v[q]);
-    }
+    for (int k = 0; k < 16; ++k) v[k] = fmaf(d, x[k], v[k]);
     if (!last) {
-      u16x4 pk;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        pk[q] = f2bf(o[q]);
-        Xz[(i0 + q) * np + j] = pk[q];
-      }
-      *(u16x4*)(XtN + int64_t(z) * mp * np + j * mp + i0) = pk;
-    } else {
-      const bool tr = tab.tr[z] != 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) NatStore::put<PT>(tab.e[z], sc, tr, m, n, i0 + q, j, o[q]);
+      Seg<uint16_t>::store(Xr, 0, 16, v);
+    } else if (!tab.tr[z]) {
+      NatStore::put_seg<PT>(tab.e[z], sc, i * n + j0, (i < m) ? clamp16(n - j0) : 0, v);
+    }
+  }
+  __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool) const {
+    if (!last) {
+      Seg<uint16_t>::store(XtN + int64_t(z) * mp * np + j * mp + i0, 0, 16, v);
+    } else if (tab.tr[z]) {
+      NatStore::put_seg<PT>(tab.e[z], sc, j * m + i0, (j < n) ? clamp16(m - i0) : 0, v);
     }
   }
 };
@@ -427,19 +528,33 @@ __global__ __launch_bounds__(TILE == 256 ? 512 : 256, TILE == 256 ? 1 : 2) void 
     }
   }
 
+  // Epilogue: each wave stages one 32 x 32 MFMA tile at a time in its own LDS
+  // slot (the operand stages are free now) and reads it back as row runs
+  // (lane l: row l/2, columns 16 (l%2) ..) and column runs.
+  __syncthreads();
+  constexpr int kLd = 36;  // slot row stride in floats
+  float* slot = reinterpret_cast<float*>(&lds[0][0][0]) + wv * (32 * kLd);
   const bool diag = upper && (ti == tj);
+  const int er = lane >> 1, ec = (lane & 1) * 16;
 #pragma unroll
   for (int a = 0; a < G::FM; ++a)
 #pragma unroll
-    for (int b = 0; b < G::FN; ++b)
+    for (int b = 0; b < G::FN; ++b) {
+      const int64_t ti0 = row0 + wr + a * 32, tj0 = col0 + wc + b * 32;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t i0 = row0 + wr + a * 32 + g * 8 + (lane >> 5) * 4;
-        const int64_t j = col0 + wc + b * 32 + (lane & 31);
-        float v[4] = {acc[a][b][g * 4 + 0], acc[a][b][g * 4 + 1], acc[a][b][g * 4 + 2],
-                      acc[a][b][g * 4 + 3]};
-        epi(z, i0, j, v, diag);
+      for (int r = 0; r < 16; ++r) slot[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kLd + (lane & 31)] = acc[a][b][r];
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = slot[er * kLd + ec + k];
+      epi.row(z, ti0 + er, tj0 + ec, v, diag);
+      if constexpr (Epi::kCol) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) slot[er * kLd + ec + k] = v[k];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = slot[(ec + k) * kLd + er];
+        epi.col(z, tj0 + er, ti0 + ec, v, diag);
       }
+    }
 }
 
 // ============================================================================

@@ -54,6 +54,51 @@ __global__ __launch_bounds__(256) void momentum_kernel(MatTable tab, StepScalars
   XT* trn = (tr ? X : Xt0) + int64_t(z) * xstride;  // transposed
   const int64_t ldn = colsP, ldt = rowsP;
   float ss = 0.f;
+  // Vector path (bf16, tile inside the matrix, 16-byte aligned rows): thread
+  // t moves 8 consecutive columns of rows t/8 and t/8 + 32 with 16-byte
+  // accesses, and 8 consecutive rows of two transposed columns.
+  if constexpr (sizeof(PT) == 2 && sizeof(XT) == 2) {
+    if (sc.mode == 0 && cols % 8 == 0 && r0 + 64 <= rows && c0 + 64 <= cols) {
+      const int cgrp = t & 7, rr = t >> 3;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int lr = rr + 32 * q;
+        const int64_t idx = (r0 + lr) * cols + c0 + 8 * cgrp;
+        const u32x4 gw = *(const u32x4*)(G + idx);
+        f32x4 m0 = *(const f32x4*)(M + idx), m1 = *(const f32x4*)(M + idx + 4);
+        float u[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float g = bf2f(uint16_t((k & 1) ? (gw[k >> 1] >> 16) : (gw[k >> 1] & 0xffffu)));
+          const float mo = (k < 4) ? m0[k] : m1[k - 4];
+          const float mn = fmaf(sc.mu, mo, g);
+          if (k < 4) m0[k] = mn; else m1[k - 4] = mn;
+          u[k] = sc.nesterov ? fmaf(sc.mu, mn, g) : mn;
+          ss = fmaf(u[k], u[k], ss);
+        }
+        *(f32x4*)(M + idx) = m0;
+        *(f32x4*)(M + idx + 4) = m1;
+        u32x4 xw;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) xw[d] = f2bf2(u[2 * d], u[2 * d + 1]);
+        *(u32x4*)(nat + (r0 + lr) * ldn + c0 + 8 * cgrp) = xw;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tileT[lr][8 * cgrp + k] = bf2f(uint16_t((k & 1) ? (xw[k >> 1] >> 16) : (xw[k >> 1] & 0xffffu)));
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int lc = rr + 32 * q;
+        u32x4 tw;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) tw[d] = f2bf2(tileT[8 * cgrp + 2 * d][lc], tileT[8 * cgrp + 2 * d + 1][lc]);
+        *(u32x4*)(trn + (c0 + lc) * ldt + r0 + 8 * cgrp) = tw;
+      }
+      const float tot = block_sum_256(ss, red);
+      if (t == 0) normpart[int64_t(z) * tiles + tile] = tot;
+      return;
+    }
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int lr = rg + 16 * q;

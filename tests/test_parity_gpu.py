@@ -97,7 +97,7 @@ def test_workload_ns_only(key):
 
 
 EDGE_SHAPES = [
-    ("skinny_ragged", [(24, 10240 + 17), (17, 1000), (1, 300), (32, 2500)], torch.bfloat16),
+    ("skinny_ragged", [(24, 10240 + 17), (17, 1000), (1, 300), (32, 2500), (28, 3001)], torch.bfloat16),
     ("skinny_tall", [(777, 20), (10240, 24)], torch.bfloat16),
     ("tiny", [(1, 1), (1, 7), (7, 1), (2, 2)], torch.bfloat16),
     ("mfma_ragged", [(33, 65), (130, 200), (300, 129), (257, 257)], torch.bfloat16),

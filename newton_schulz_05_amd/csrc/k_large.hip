@@ -264,7 +264,7 @@ struct NatStore {
       return;
     }
     PT* W = (PT*)r.w + idx0;
-    float w[16];
+    float w[16] = {};
     Seg<PT>::load(W, 0, cnt, w);
     const float keep = 1.0f - sc.lr * sc.wd;
 #pragma unroll

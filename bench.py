@@ -144,6 +144,50 @@ def bench_adamw(steps, warmup, elems):
                          "launches_per_step": (len(sizes) + 31) // 32}}
 
 
+def time_groups(wl, steps, warmup, dev):
+    """Each shape group of a multi-group workload timed alone (its own plan
+    over the parameters of that group), with the fraction of its own bound:
+    HBM for skinny bf16 groups (m <= 32), bf16 MFMA otherwise."""
+    import torch
+    from newton_schulz_05_amd import MuonPlan
+    from newton_schulz_05_amd import workloads as WL
+    keys = []
+    for s in wl.shapes:
+        k = (min(s[-2:]), max(s[-2:]))
+        if k not in keys:
+            keys.append(k)
+    out = []
+    for k in keys:
+        idx = [i for i, s in enumerate(wl.shapes) if (min(s[-2:]), max(s[-2:])) == k]
+        sub = type(wl)(wl.key, wl.number, wl.name, tuple(wl.shapes[i] for i in idx), wl.dtype, wl.g_std)
+        plan = MuonPlan(sub.shapes, sub.dtype)
+        ws = plan.new_workspace(dev)
+        ps = [WL.make_params(wl, dev, dev)[i] for i in idx]
+        ms_ = [torch.zeros(tuple(wl.shapes[i]), dtype=torch.float32, device=dev) for i in idx]
+        gs = [[WL.make_grads(wl, t, dev, dev)[i] for i in idx] for t in range(2)]
+        bound = [plan.bind(ps, g, ms_, workspace=ws) for g in gs]
+        st = torch.cuda.current_stream()
+        hyper = wl.hyper()
+        step = [0]
+
+        def fn():
+            bound[step[0] % 2].step(**hyper, stream=st)
+            step[0] += 1
+        ms = _events_time(fn, steps, warmup, st)
+        skinny = k[0] <= 32 and wl.dtype == torch.bfloat16
+        if skinny:
+            gbs = alg_bytes(sub) / (ms * 1e-3) / 1e9
+            frac = {"bound": "hbm", "achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        else:
+            tf = alg_flops(sub) / (ms * 1e-3) / 1e12
+            frac = {"bound": "mfma", "achieved": round(tf, 1), "unit": "TFLOP/s",
+                    "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        out.append({"group": f"{sub.n_matrices()} x [{k[0]}, {k[1]}]", "ms_per_step": round(ms, 5), **frac})
+        del plan, ws, ps, ms_, gs, bound
+        torch.cuda.empty_cache()
+    return out
+
+
 def alg_flops(wl) -> float:
     """3 m^2 n + m^3 per matrix per NS iteration (Gram exploits symmetry)."""
     tot = 0.0
@@ -286,6 +330,10 @@ def main() -> int:
         roof = {"bound": "alu", "achieved": round(tflops, 3), "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / F32_VALU_PEAK_TFLOPS, 6), "traffic": None, "kernel": "whole step"}
 
+    per_group = None
+    if len(groups) > 1:
+        per_group = time_groups(wl, steps, warmup, dev)
+
     out = {
         "metric": "Muon step ms & TFLOP/s (% bf16 MFMA peak / % HBM BW) for batched NS on [B,M,N]",
         "value": round(tflops, 3),
@@ -307,6 +355,8 @@ def main() -> int:
                    "parallelism": "single_gpu"},
         "roofline": roof,
     }
+    if per_group is not None:
+        out["groups"] = per_group
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl if not big else WL.custom([wl.shapes[0]], dtype=wl.dtype,
                                                                         g_std=wl.g_std, number=wl.number),

@@ -99,9 +99,9 @@ muon_status muon_plan_num_groups(muon_plan plan, int32_t* n_groups);
 muon_status muon_plan_group_info(muon_plan plan, int32_t g, int64_t* m, int64_t* n,
                                  int64_t* count, int64_t* n_transposed, int64_t* n_chunks);
 
-/* The workspace must be zero-filled once before its first use with any plan
- * (a small region of it holds cross-workgroup barrier counters that every
- * completed call leaves at zero). */
+/* The workspace must be zero-filled once before its first use with any plan:
+ * a small region of it holds the tagged words the skinny kernel's workgroups
+ * exchange and a timeout flag, and an all-zero word carries no valid tag. */
 
 /* One Muon step on every parameter of the plan (see the formulas above).
  *   param_ptrs : W, updated in place, dtype param_dt.
@@ -196,6 +196,23 @@ muon_status muon_adamw_step(void* const* params, const void* const* grads, float
                             float* const* exp_avg_sq, const int64_t* numels, int32_t n, muon_dtype dt,
                             float lr, float b1, float b2, float eps, float wd, int64_t step,
                             void* stream);
+
+/* ---- Diagnostics of the skinny path ---------------------------------------
+ * Its cross-workgroup waits are bounded.  If one times out (the co-residency
+ * the launch relies on was not granted, or the wait limit is too small), the
+ * kernel raises a flag in the workspace, still runs to completion, and the
+ * results of that call are invalid. */
+
+/* Synchronises `stream` (the host waits for it), sets *timed_out to 1 if any
+ * call on this workspace timed out since the last check, else 0, and clears
+ * the flag.  Not for use inside graph capture. */
+muon_status muon_workspace_status(muon_plan plan, void* workspace, size_t workspace_bytes, void* stream,
+                                  int32_t* timed_out);
+
+/* Polls a waiting workgroup makes before it gives up, for the launches that
+ * follow in this process (default 1048576, about a second; 0 restores the
+ * default).  Meant for tests of the timeout path. */
+void muon_set_wait_limit(uint32_t polls);
 
 const char* muon_status_str(muon_status s);
 const char* muon_last_error_detail(void);

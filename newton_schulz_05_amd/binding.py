@@ -33,6 +33,7 @@ STATUS = {
 EXPORTS = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes",
            "muon_plan_num_groups", "muon_plan_group_info", "muon_step", "muon_ns",
            "muon_plan_num_matrices", "muon_plan_assign", "muon_shard_update", "muon_adamw_step",
+           "muon_workspace_status", "muon_set_wait_limit",
            "muon_status_str", "muon_last_error_detail", "muon_version"]
 
 
@@ -89,6 +90,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_shard_update.restype = i32
     lib.muon_adamw_step.argtypes = [P(vp), P(vp), P(vp), P(vp), P(i64), i32, i32, f32, f32, f32, f32, f32, i64, vp]
     lib.muon_adamw_step.restype = i32
+    lib.muon_workspace_status.argtypes = [vp, vp, sz, vp, P(i32)]
+    lib.muon_workspace_status.restype = i32
+    lib.muon_set_wait_limit.argtypes = [ctypes.c_uint32]
+    lib.muon_set_wait_limit.restype = None
     lib.muon_status_str.argtypes = [i32]
     lib.muon_status_str.restype = ctypes.c_char_p
     lib.muon_last_error_detail.argtypes = []
@@ -193,6 +198,15 @@ class MuonPlan:
         cost = (ctypes.c_double * max(int(n_ranks), 1))()
         _check(load_library().muon_plan_assign(self._h, int(n_ranks), owner, nm, cost))
         return [int(owner[j]) for j in range(nm)], [float(cost[r]) for r in range(int(n_ranks))]
+
+    def workspace_timed_out(self, workspace: torch.Tensor, stream=None) -> bool:
+        """Synchronise the stream and report (and clear) the skinny path's
+        timeout flag in `workspace` (muon_workspace_status)."""
+        flag = ctypes.c_int32()
+        _check(load_library().muon_workspace_status(self._h, ctypes.c_void_p(workspace.data_ptr()),
+                                                    workspace.numel(), ctypes.c_void_p(self._stream(stream)),
+                                                    ctypes.byref(flag)))
+        return bool(flag.value)
 
     def new_workspace(self, device="cuda") -> torch.Tensor:
         """Zero-filled workspace of the plan's size (a torch uint8 tensor)."""
@@ -343,3 +357,9 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr: float, betas=(0.9, 0
     params/grads share a dtype (bf16 or fp32); the moment buffers are fp32."""
     AdamWGroup(params, grads, exp_avgs, exp_avg_sqs).step(lr=lr, betas=betas, eps=eps, wd=wd, step=step,
                                                           stream=stream)
+
+
+def set_wait_limit(polls: int) -> None:
+    """Polls before a waiting workgroup of the skinny kernel gives up
+    (muon_set_wait_limit; 0 restores the default)."""
+    load_library().muon_set_wait_limit(int(polls))

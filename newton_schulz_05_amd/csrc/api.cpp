@@ -28,6 +28,7 @@ muon_status fail(muon_status s, const std::string& d) {
 }
 
 constexpr unsigned kSpinLimit = 1u << 20;  // bounded barrier wait (polls, about a second)
+std::atomic<unsigned> g_spin_limit{kSpinLimit};
 
 // Distinct number per skinny launch (modulo 2^27): tags the kernel's published
 // partials, so words left by an earlier launch in the same workspace are never
@@ -128,7 +129,7 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         a.slab_w = grp.slab_w;
         a.part = (float*)(ws + P.ws_dyn_off);
         a.sync = (uint32_t*)(ws + P.ws_sync_off);
-        a.spin_limit = kSpinLimit;
+        a.spin_limit = g_spin_limit.load();
         a.epoch = next_epoch();
         e = run_skinny(a, st);
       } else {
@@ -315,6 +316,30 @@ muon_status muon_adamw_step(void* const* params, const void* const* grads, float
   if (hipError_t e = flush(); e != hipSuccess) return fail(MUON_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return MUON_OK;
 }
+
+muon_status muon_workspace_status(muon_plan plan, void* workspace, size_t workspace_bytes, void* stream,
+                                  int32_t* timed_out) {
+  if (!plan || !timed_out) return fail(MUON_ERR_INVALID_ARG, "null plan or output pointer");
+  const muon::Plan& P = plan->p;
+  muon_status s = check_workspace(P, workspace, workspace_bytes);
+  if (s != MUON_OK) return s;
+  const hipStream_t st = (hipStream_t)stream;
+  uint32_t* flag = (uint32_t*)((uint8_t*)workspace + P.ws_sync_off) + muon::kSyncErrWord;
+  uint32_t h = 0;
+  if (hipMemcpyAsync(&h, flag, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return fail(MUON_ERR_HIP, "reading the workspace flag failed");
+  *timed_out = h ? 1 : 0;
+  if (h) {
+    const uint32_t zero = 0;
+    if (hipMemcpyAsync(flag, &zero, sizeof(zero), hipMemcpyHostToDevice, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return fail(MUON_ERR_HIP, "clearing the workspace flag failed");
+  }
+  return MUON_OK;
+}
+
+void muon_set_wait_limit(uint32_t polls) { g_spin_limit.store(polls ? polls : kSpinLimit); }
 
 muon_status muon_step(muon_plan plan, void* const* param_ptrs, const void* const* grad_ptrs,
                       void* const* mom_ptrs, const muon_shape* shapes, int32_t n_params, float lr,

@@ -41,7 +41,6 @@ namespace {
 constexpr int kNB = 8;            // 32-column blocks per wave (slab <= 4 * 8 * 32 = 1024 columns)
 constexpr int kLdr = 36;          // LDS column stride (bf16) of the transpose staging
 constexpr int kPartW = 544;       // 8-byte words per published slab partial (upper triangle <= 528, + sum of squares)
-constexpr int kErrSlot = 2040;    // u32 index of the timeout flag in the sync region
 constexpr int kCoherent = 16;     // buffer cache policy: device-coherent access (sc1)
 constexpr int kGather = 12;       // partial words each thread has in flight while gathering
 
@@ -380,7 +379,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
         for (int j = 0; j < kGather; ++j) ready &= (t + 256 * j >= tot) || (w[j][1] == tag);
         if (ready) break;
         if (++it > spin_limit) {
-          __hip_atomic_store(sync + kErrSlot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(sync + kSyncErrWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
         __builtin_amdgcn_s_sleep(1);

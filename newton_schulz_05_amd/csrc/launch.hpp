@@ -20,6 +20,9 @@ struct LargeArgs {
   bool bf16;
 };
 
+// u32 index, in the workspace's sync region, of the skinny path's timeout flag
+constexpr int kSyncErrWord = 2040;
+
 // One chunk of the persistent skinny path.
 struct SkinnyArgs {
   MatTable tab;

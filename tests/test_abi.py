@@ -134,3 +134,14 @@ def test_shard_update_rejects_bad_calls_before_launch():
     assert lib.muon_shard_update(ctypes.c_void_p(0x900010), B.MUON_F32, fake_o, 0, 64, 0.1, 0.0, 1.0, None) == 1
     # len = 0 enqueues nothing and succeeds
     assert lib.muon_shard_update(fake_w, B.MUON_BF16, fake_o, 5, 0, 0.1, 0.0, 1.0, None) == 0
+
+
+def test_workspace_status_rejects_bad_calls_before_touching_the_device():
+    lib = B.load_library()
+    flag = ctypes.c_int32(7)
+    assert lib.muon_workspace_status(None, ctypes.c_void_p(0x1000), 1 << 20, None, ctypes.byref(flag)) == 1
+    plan = B.MuonPlan([(24, 1000)], B.torch.bfloat16)
+    assert lib.muon_workspace_status(plan._h, None, plan.workspace_bytes, None, ctypes.byref(flag)) == 5
+    assert lib.muon_workspace_status(plan._h, ctypes.c_void_p(0x1000), 16, None, ctypes.byref(flag)) == 5
+    assert flag.value == 7
+    lib.muon_set_wait_limit(0)  # restores the default; callable without a device

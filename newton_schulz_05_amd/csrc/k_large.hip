@@ -6,8 +6,9 @@
 //   momentum_kernel   M <- mu*M + G; U = G + mu*M (or M); writes U into X and
 //                     Xt in the NS storage type and per-tile sums of U^2
 //   norm_kernel       s = 1 / (||U||_F + eps) per matrix, fixed-order sum
-//   gram (MFMA)       A = sc * X X^T on upper tiles, mirrored; also H = bf16(A)
-//                     and L = bf16(A - H) for the split A^2
+//   gram (MFMA)       A = sc * X X^T on upper tiles (fp32, upper tiles only);
+//                     H = bf16(A) and L = bf16(A - H) for the split A^2,
+//                     mirrored to full matrices (they are GEMM operands)
 //   poly (MFMA)       S = H H + H L + L H  (A^2 to ~16 mantissa bits), then
 //                     P = ps * (a I + b A + c S); stores the off-diagonal part
 //                     in bf16 and the diagonal in fp32

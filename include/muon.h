@@ -115,7 +115,11 @@ muon_status muon_plan_group_info(muon_plan plan, int32_t g, int64_t* m, int64_t*
  *                256-byte aligned, zero-filled once before first use.
  * Tensor results do not depend on how matrices are grouped or batched:
  * every matrix is computed with the same tiling and reduction order
- * whatever its batch, position or group. */
+ * whatever its batch, position or group.
+ * The call may be recorded into a HIP graph (stream capture): it enqueues
+ * kernels only.  Recorded skinny launches are numbered by a counter in the
+ * workspace, so replays and eager calls can share one workspace, one at a
+ * time. */
 muon_status muon_step(muon_plan plan, void* const* param_ptrs, const void* const* grad_ptrs,
                       void* const* mom_ptrs, const muon_shape* shapes, int32_t n_params,
                       float lr, float mu, int32_t nesterov, float wd, float a, float b,

@@ -30,15 +30,22 @@ muon_status fail(muon_status s, const std::string& d) {
 constexpr unsigned kSpinLimit = 1u << 20;  // bounded barrier wait (polls, about a second)
 std::atomic<unsigned> g_spin_limit{kSpinLimit};
 
-// Distinct number per skinny launch (modulo 2^27): tags the kernel's published
+// Distinct number per skinny launch (modulo 2^26): tags the kernel's published
 // partials, so words left by an earlier launch in the same workspace are never
-// mistaken for new ones.
+// mistaken for new ones.  Launches recorded into a graph are numbered on the
+// device instead (kDeviceEpochBit range), since a replay repeats the kernel
+// arguments.
 std::atomic<uint32_t> g_epoch{1};
 
 uint32_t next_epoch() {
-  uint32_t e = g_epoch.fetch_add(1) & ((1u << 27) - 1);
-  if (e == 0) e = g_epoch.fetch_add(1) & ((1u << 27) - 1);  // tag 0 marks unwritten words
+  uint32_t e = g_epoch.fetch_add(1) & (muon::kDeviceEpochBit - 1);
+  if (e == 0) e = g_epoch.fetch_add(1) & (muon::kDeviceEpochBit - 1);  // tag 0 marks unwritten words
   return e;
+}
+
+bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
 }
 
 // Co-resident workgroup capacity of the skinny kernel, per device id.
@@ -117,7 +124,7 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         tab.e[q].m = m ? (float*)m[me.param] + off : nullptr;
         tab.tr[q] = me.tr ? 1 : 0;
       }
-      hipError_t e;
+      hipError_t e = hipSuccess;
       if (grp.path == PATH_SKINNY) {
         SkinnyArgs a;
         a.tab = tab;
@@ -130,8 +137,16 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         a.part = (float*)(ws + P.ws_dyn_off);
         a.sync = (uint32_t*)(ws + P.ws_sync_off);
         a.spin_limit = g_spin_limit.load();
-        a.epoch = next_epoch();
-        e = run_skinny(a, st);
+        a.epoch = 0;
+        a.epoch_dev = nullptr;
+        if (capturing(st)) {
+          uint32_t* counter = a.sync + muon::kSyncEpochWord;
+          e = muon::run_epoch_bump(counter, st);
+          a.epoch_dev = counter;
+        } else {
+          a.epoch = next_epoch();
+        }
+        if (e == hipSuccess) e = run_skinny(a, st);
       } else {
         LargeArgs a;
         a.tab = tab;

@@ -169,8 +169,11 @@ template <typename PT, int MODE, int KS>
 __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalars sc, int m, int64_t n,
                                                         int S, int64_t slab_w, float* __restrict__ part,
                                                         uint32_t* __restrict__ sync, unsigned spin_limit,
-                                                        uint32_t epoch) {
+                                                        uint32_t epoch_host, const uint32_t* __restrict__ epoch_dev) {
   static_assert(sizeof(PT) == 2, "skinny path is bf16");
+  // launches recorded into a graph read their number from the counter that
+  // the one-thread kernel before them advanced; others get it from the host
+  const uint32_t epoch = epoch_dev ? (kDeviceEpochBit | (*epoch_dev & (kDeviceEpochBit - 1))) : epoch_host;
   constexpr bool step_mode = MODE == 0;
   __shared__ SkShared sh;
   const int z = blockIdx.x / S, s = blockIdx.x % S;
@@ -555,7 +558,7 @@ template <int MODE, int KS>
 static void launch_skinny(const SkinnyArgs& g, hipStream_t st) {
   const unsigned grid = unsigned(g.count * g.slabs);
   hipLaunchKernelGGL((skinny_kernel<uint16_t, MODE, KS>), dim3(grid), dim3(256), 0, st, g.tab, g.sc, g.m, g.n,
-                     g.slabs, g.slab_w, g.part, g.sync, g.spin_limit, g.epoch);
+                     g.slabs, g.slab_w, g.part, g.sync, g.spin_limit, g.epoch, g.epoch_dev);
 }
 
 hipError_t run_skinny(const SkinnyArgs& g, hipStream_t st) {
@@ -565,6 +568,13 @@ hipError_t run_skinny(const SkinnyArgs& g, hipStream_t st) {
   } else {
     if (small) launch_skinny<1, 6>(g, st); else launch_skinny<1, 8>(g, st);
   }
+  return hipGetLastError();
+}
+
+__global__ void epoch_bump_kernel(uint32_t* c) { *c = *c + 1u; }
+
+hipError_t run_epoch_bump(uint32_t* counter, hipStream_t st) {
+  hipLaunchKernelGGL(epoch_bump_kernel, dim3(1), dim3(1), 0, st, counter);
   return hipGetLastError();
 }
 

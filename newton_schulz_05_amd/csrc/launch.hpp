@@ -20,8 +20,13 @@ struct LargeArgs {
   bool bf16;
 };
 
-// u32 index, in the workspace's sync region, of the skinny path's timeout flag
+// u32 indices, in the workspace's sync region, of the skinny path's timeout
+// flag and of the launch counter that numbers launches recorded into a graph
 constexpr int kSyncErrWord = 2040;
+constexpr int kSyncEpochWord = 2044;
+// Exchange epochs: launches numbered on the host take [1, 2^26); launches
+// numbered by the device counter (graph capture) take 2^26 + (count mod 2^26).
+constexpr uint32_t kDeviceEpochBit = 1u << 26;
 
 // One chunk of the persistent skinny path.
 struct SkinnyArgs {
@@ -35,12 +40,15 @@ struct SkinnyArgs {
   float* part;       // published slab partials
   uint32_t* sync;    // timeout flag
   unsigned spin_limit;
-  uint32_t epoch;    // distinct per call: tags the published partials
+  uint32_t epoch;    // distinct per launch: tags the published partials
+  const uint32_t* epoch_dev;  // if set, the epoch is read from here (graph capture)
 };
 
 hipError_t run_large(const LargeArgs& a, hipStream_t st);
 hipError_t run_skinny(const SkinnyArgs& a, hipStream_t st);
 int skinny_max_blocks_per_cu();
+// one-thread kernel: counter <- counter + 1 (numbers the next skinny launch)
+hipError_t run_epoch_bump(uint32_t* counter, hipStream_t st);
 
 // W[i] <- W[i] (1 - lr wd) - lr scale O[i], i < len (one rank's shard of a parameter).
 hipError_t run_shard_update(void* w, bool bf16, const float* o, int64_t len, float lr, float wd, float scale,

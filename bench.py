@@ -188,6 +188,33 @@ def time_groups(wl, steps, warmup, dev):
     return out
 
 
+def bench_ns(wl, steps, warmup):
+    """muon_ns alone (NS of every matrix, O in fp32) on the workload's
+    gradients, for the NS-only comparison with the pages' figures."""
+    import torch
+    from newton_schulz_05_amd import MuonPlan
+    from newton_schulz_05_amd import workloads as WL
+    plan = MuonPlan(wl.shapes, wl.dtype)
+    ws = plan.new_workspace("cuda")
+    ins = WL.make_grads(wl, 0, "cuda", "cuda")
+    outs = [torch.empty(tuple(s), dtype=torch.float32, device="cuda") for s in wl.shapes]
+    st = torch.cuda.current_stream()
+
+    bound = plan.bind_ns(ins, outs, workspace=ws)
+
+    def fn():
+        bound.ns(coeffs=wl.coeffs, ns_steps=wl.ns_steps, stream=st)
+    ms = _events_time(fn, steps, warmup, st)
+    tf = alg_flops(wl) / (ms * 1e-3) / 1e12
+    context = {"c2": "74 x [24, 10240] NS, fused [74, 24, 10240] batch on the pages' Ascend NPU: 2.4 ms"}
+    return {"metric": "muon_ns ms per call (NS only)", "value": round(ms, 5), "unit": "ms", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": False,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+            "data": "synthetic", "config": {"workload": wl.name, "matrices": wl.n_matrices(),
+                                            "alg_tflop_per_call": alg_flops(wl) / 1e12},
+            "tflops_alg": round(tf, 3), "context": context.get(wl.key)}
+
+
 def alg_flops(wl) -> float:
     """3 m^2 n + m^3 per matrix per NS iteration (Gram exploits symmetry)."""
     tot = 0.0
@@ -251,8 +278,9 @@ def main() -> int:
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="step", choices=["step", "shard_update", "adamw"],
-                    help="step: the Muon step (default); shard_update / adamw: the companion kernels")
+    ap.add_argument("--op", default="step", choices=["step", "ns", "shard_update", "adamw"],
+                    help="step: the Muon step (default); ns: muon_ns alone on the workload; "
+                         "shard_update / adamw: the companion kernels")
     ap.add_argument("--adamw-elems", type=int, default=0,
                     help="adamw: total elements of a 64-tensor stress set instead of the model's gains")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -265,6 +293,13 @@ def main() -> int:
 
     if args.copy_probe:
         return copy_probe(args.copy_probe, args.steps or 5)
+    if args.op == "ns":
+        from newton_schulz_05_amd import workloads as WL
+        wl = WL.WORKLOADS[args.config]
+        big = args.config in ("c4", "c5")
+        print(json.dumps(bench_ns(wl, args.steps or (5 if big else 100), args.warmup or (1 if big else 10))),
+              flush=True)
+        return 0
     if args.op == "shard_update":
         print(json.dumps(bench_shard_update(args.steps or 50, args.warmup or 5)), flush=True)
         return 0

@@ -269,6 +269,14 @@ class MuonPlan:
             workspace = self._default_ws(params[0].device)
         return BoundStep(self, params, grads, moms, workspace)
 
+    def bind_ns(self, inputs, outputs, *, workspace: Optional[torch.Tensor] = None) -> "BoundNS":
+        """Validate NS inputs and fp32 outputs once (see bind)."""
+        self._check_tensors(inputs, self.dtype, "inputs")
+        self._check_tensors(outputs, torch.float32, "outputs")
+        if workspace is None:
+            workspace = self._default_ws(inputs[0].device)
+        return BoundNS(self, inputs, outputs, workspace)
+
     def _default_ws(self, device) -> torch.Tensor:
         ws = getattr(self, "_ws", None)
         if ws is None or ws.device != device:
@@ -363,3 +371,21 @@ def set_wait_limit(polls: int) -> None:
     """Polls before a waiting workgroup of the skinny kernel gives up
     (muon_set_wait_limit; 0 restores the default)."""
     load_library().muon_set_wait_limit(int(polls))
+
+
+class BoundNS:
+    """muon_ns over a fixed set of tensors (see MuonPlan.bind_ns)."""
+
+    def __init__(self, plan: MuonPlan, inputs, outputs, workspace: torch.Tensor):
+        self.plan = plan
+        self._keep = (list(inputs), list(outputs), workspace)
+        self._i, self._o = _ptrs(inputs), _ptrs(outputs)
+        self._ws = ctypes.c_void_p(workspace.data_ptr())
+        self._ws_bytes = workspace.numel()
+        self._lib = load_library()
+
+    def ns(self, *, coeffs=(3.4445, -4.7750, 2.0315), ns_steps: int = 5, stream=None) -> None:
+        a, b, c = coeffs
+        _check(self._lib.muon_ns(self.plan._h, self._i, self._o, self.plan._cshapes, len(self.plan.shapes),
+                                 a, b, c, ns_steps, self._ws, self._ws_bytes,
+                                 ctypes.c_void_p(MuonPlan._stream(stream))))

@@ -129,3 +129,16 @@ def test_gemm_tile_choice_is_bitwise_neutral():
         p1, m1 = _step([shapes[i]], [params[i].clone()], [[grads[0][i]], [grads[1][i]]], torch.bfloat16)
         assert torch.equal(p1[0], pg[i]), f"W[{i}] differs between the 128 and 256 tile kernels"
         assert torch.equal(m1[0], mg[i])
+
+
+def test_bound_ns_equals_ns():
+    shapes = [(24, 3000)] * 3 + [(96, 640)]
+    wl = WL.custom(shapes, number=76)
+    ins = WL.make_grads(wl, 0, DEV, "cpu")
+    plan = MuonPlan(shapes, torch.bfloat16)
+    o1 = [torch.empty(s, dtype=torch.float32, device=DEV) for s in shapes]
+    o2 = [torch.empty(s, dtype=torch.float32, device=DEV) for s in shapes]
+    plan.ns(ins, o1)
+    plan.bind_ns(ins, o2).ns()
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(o1, o2))

@@ -35,9 +35,9 @@ F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 # only for the kernel source it was taken on (SHA-256 of k_skinny.hip);
 # otherwise `traffic` is reported as null.
 SKINNY_TRAFFIC = {
-    "kernel_source_sha256": "ac54d5f7f334f5b3f556b2c41832e4be53a4ffccfe5ca5969429a0d9dbe4d03c",
-    "fetch_kib_per_dispatch": 83041.5,
-    "write_kib_per_dispatch": 109318.4,
+    "kernel_source_sha256": "98284fed7dda61e39386a336ed8957e3b30cc7eb74cea5b2512e3e5798d09510",
+    "fetch_kib_per_dispatch": 83141.0,
+    "write_kib_per_dispatch": 109317.9,
     "fetch_scale": 2.0,      # 262144 KiB copied / 131085.5 KiB counted
     "write_scale": 1.0,      # 262144 KiB copied / 262144.0 KiB counted
 }

@@ -256,6 +256,10 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       for (int i = 0; i < 4; ++i) pm[q & 1][i] = buf_ld_b128(rM, e0 * 4 + 16 * i);
     }
   };
+  // Wave priorities order the phases that share a SIMD: the latency-bound
+  // exchange and Gram-space recurrence (3) before the momentum streaming (2)
+  // before the weight update (0).
+  __builtin_amdgcn_s_setprio(2);
   if (full(0)) issue(0);
 #pragma unroll
   for (int q = 0; q < kNB; ++q) {
@@ -539,10 +543,12 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   };
 
   // ---- Gram of X0, one exchange, Gram-space NS, apply and update ------------
+  __builtin_amdgcn_s_setprio(3);
   publish(gacc, 0, true);
   float snorm = 1.f;
   gather_a(0, true, snorm);
   gram_space_ns(snorm);
+  __builtin_amdgcn_s_setprio(0);
   {
     const int lane = opaque(int(threadIdx.x)) & 63;
 #pragma unroll

@@ -145,3 +145,27 @@ def test_workspace_status_rejects_bad_calls_before_touching_the_device():
     assert lib.muon_workspace_status(plan._h, ctypes.c_void_p(0x1000), 16, None, ctypes.byref(flag)) == 5
     assert flag.value == 7
     lib.muon_set_wait_limit(0)  # restores the default; callable without a device
+
+
+def test_adamw_rejects_bad_calls_before_launch():
+    lib = B.load_library()
+    P = ctypes.c_void_p
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    p, g, m, v = arr(0x1000), arr(0x2000), arr(0x3000), arr(0x4000)
+    n1 = (ctypes.c_int64 * 1)(16)
+
+    def call(n=1, dt=B.MUON_F32, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, step=1, numels=n1, pp=p):
+        return lib.muon_adamw_step(pp, g, m, v, numels, n, dt, lr, b1, b2, eps, wd, step, None)
+
+    assert call(dt=5) == 3
+    assert call(n=-1) == 1
+    assert call(b1=1.0) == 1
+    assert call(b2=-0.1) == 1
+    assert call(eps=0.0) == 1
+    assert call(step=0) == 1
+    assert call(lr=float("inf")) == 1
+    assert call(numels=(ctypes.c_int64 * 1)(-3)) == 2
+    assert call(pp=arr(0x1002)) == 7          # not 4-byte aligned
+    assert call(pp=arr(None)) == 1
+    assert call(n=0) == 0                     # nothing to do
+    assert call(numels=(ctypes.c_int64 * 1)(0)) == 0

@@ -208,6 +208,21 @@ class MuonPlan:
                                                     ctypes.byref(flag)))
         return bool(flag.value)
 
+    def rank_views(self, tensors: Sequence[torch.Tensor], owner: Sequence[int], rank: int) -> List[torch.Tensor]:
+        """The matrices that `owner` (from assign) gives to `rank`, as 2-D
+        views of `tensors` (a parameter, or one slice of an expert slab), in
+        plan order.  A plan built over their shapes steps exactly those
+        matrices in place."""
+        mats = self.matrices()
+        if len(owner) != len(mats):
+            raise MuonError(1, f"owner has {len(owner)} entries for {len(mats)} matrices")
+        out = []
+        for (i, e), o in zip(mats, owner):
+            if o == rank:
+                t = tensors[i]
+                out.append(t[e] if t.dim() == 3 else t)
+        return out
+
     def new_workspace(self, device="cuda") -> torch.Tensor:
         """Zero-filled workspace of the plan's size (a torch uint8 tensor)."""
         return torch.zeros(self.workspace_bytes, dtype=torch.uint8, device=device)

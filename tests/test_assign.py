@@ -126,3 +126,15 @@ def test_two_gloo_ranks_compute_the_same_split(tmp_path):
     mp.spawn(_rank_main, args=(2, _free_port(), str(tmp_path)), nprocs=2, join=True)
     for r in range(2):
         assert (tmp_path / f"rank{r}").read_text() == "ok"
+
+
+def test_rank_views_cover_each_matrix_once():
+    shapes = [(64, 128), (3, 32, 48), (100, 40)]
+    plan = MuonPlan(shapes)
+    ts = [torch.zeros(s) for s in shapes]
+    owner, _ = plan.assign(2)
+    views = [plan.rank_views(ts, owner, r) for r in range(2)]
+    assert sum(len(v) for v in views) == plan.num_matrices()
+    for v in views[0] + views[1]:
+        v.add_(1.0)
+    assert all(bool((t == 1.0).all()) for t in ts)

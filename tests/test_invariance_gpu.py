@@ -142,3 +142,30 @@ def test_bound_ns_equals_ns():
     plan.bind_ns(ins, o2).ns()
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(o1, o2))
+
+
+def test_ranks_stepping_their_assigned_matrices_reproduce_the_full_step():
+    """The de-duplicated split on one device: each of 3 simulated ranks steps
+    only the matrices muon_plan_assign gives it (its own plan over 2-D views,
+    expert slices included); together they must reproduce the single
+    full-set step bit for bit."""
+    shapes = [(4, 96, 160), (24, 3000), (24, 3000), (200, 96), (96, 200), (2, 24, 1000)]
+    params, grads = _draw(shapes, torch.bfloat16, 77)
+    full_p, full_m = _step(shapes, [p.clone() for p in params], grads, torch.bfloat16)
+    plan = MuonPlan(shapes, torch.bfloat16)
+    owner, _ = plan.assign(3)
+    p_split = [p.clone() for p in params]
+    m_split = [torch.zeros(p.shape, dtype=torch.float32, device=DEV) for p in params]
+    for r in range(3):
+        pv = plan.rank_views(p_split, owner, r)
+        if not pv:
+            continue
+        mv = plan.rank_views(m_split, owner, r)
+        sub = MuonPlan([tuple(v.shape) for v in pv], torch.bfloat16)
+        for s in range(2):
+            gv = plan.rank_views(grads[s], owner, r)
+            sub.step(pv, gv, mv, lr=0.02, wd=0.1)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.equal(p_split[i], full_p[i]), f"W[{i}]"
+        assert torch.equal(m_split[i], full_m[i]), f"M[{i}]"

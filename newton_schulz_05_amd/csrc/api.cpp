@@ -48,22 +48,30 @@ bool capturing(hipStream_t st) {
   return hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
 }
 
-// Co-resident workgroup capacity of the skinny kernel, per device id.
-std::mutex g_cap_mu;
-std::vector<int> g_cap;  // -1 = not queried
+// Compute-unit count of the current device, per device id.
+std::mutex g_cu_mu;
+std::vector<int> g_cus;  // -1 = not queried
 
-muon_status skinny_capacity(int* cap) {
+muon_status device_cus(int* cus) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
-  std::lock_guard<std::mutex> lk(g_cap_mu);
-  if (int(g_cap.size()) <= dev) g_cap.resize(dev + 1, -1);
-  if (g_cap[dev] < 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+  std::lock_guard<std::mutex> lk(g_cu_mu);
+  if (int(g_cus.size()) <= dev) g_cus.resize(dev + 1, -1);
+  if (g_cus[dev] < 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       return fail(MUON_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
-    g_cap[dev] = cus * muon::skinny_max_blocks_per_cu();
+    g_cus[dev] = n;
   }
-  *cap = g_cap[dev];
+  *cus = g_cus[dev];
+  return MUON_OK;
+}
+
+// Co-resident workgroup capacity of the skinny kernel on the current device.
+muon_status skinny_capacity(int* cap) {
+  int cus = 0;
+  if (muon_status s = device_cus(&cus); s != MUON_OK) return s;
+  *cap = cus * muon::skinny_max_blocks_per_cu();
   return MUON_OK;
 }
 
@@ -160,6 +168,7 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         a.np = grp.np;
         a.tile = grp.tile;
         a.bf16 = (grp.path == PATH_MFMA);
+        if (muon_status s = device_cus(&a.cus); s != MUON_OK) return s;
         e = run_large(a, st);
       }
       if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));

@@ -473,7 +473,7 @@ template <int TILE, int NPROD, typename Epi>
 __global__ __launch_bounds__(TILE == 256 ? 512 : 256, TILE == 256 ? 1 : 2) void gemm_bf16_kernel(
     const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al, int64_t lda, int64_t sA,
     const uint16_t* __restrict__ Bh, const uint16_t* __restrict__ Bl, int64_t ldb, int64_t sB,
-    int64_t K, int tilesN, int upper, Epi epi) {
+    int64_t K, int tilesN, int upper, int per, int base, int split, Epi epi) {
   using G = GemmGeom<TILE>;
   constexpr int NA = (NPROD == 3) ? 2 : 1;      // operand planes per side
   constexpr int BK = (NPROD == 3) ? 32 : 64;
@@ -483,9 +483,20 @@ __global__ __launch_bounds__(TILE == 256 ? 512 : 256, TILE == 256 ? 1 : 2) void 
   constexpr int LP = PLANE / G::NT;             // loads per thread per plane
   constexpr int KS = BK / 16;
   __shared__ u16x8 lds[2][2 * NA][PLANE];       // [stage][Ah, (Al), Bh, (Bl)]
-  const int z = blockIdx.y;
+  // Work item f = matrix * per + tile, in units of the tiles that tilesN
+  // counts.  With split, each such tile (twice TILE on a side) is done by four
+  // workgroups, one per TILE-quarter; a symmetric output skips the quarter
+  // below the diagonal.
+  const int f = base + (split ? int(blockIdx.x >> 2) : int(blockIdx.x));
+  const int z = f / per;
   int ti, tj;
-  tile_coords(blockIdx.x, tilesN, upper != 0, ti, tj);
+  tile_coords(f - z * per, tilesN, upper != 0, ti, tj);
+  if (split) {
+    const int q = int(blockIdx.x & 3);
+    ti = 2 * ti + (q >> 1);
+    tj = 2 * tj + (q & 1);
+    if (upper && ti > tj) return;
+  }
   const int64_t row0 = int64_t(ti) * TILE, col0 = int64_t(tj) * TILE;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int wr = (wv / G::WN) * G::TMW, wc = (wv % G::WN) * G::TNW;
@@ -672,10 +683,38 @@ __global__ __launch_bounds__(256) void ns0_kernel(MatTable tab, StepScalars sc, 
 // ============================================================================
 static hipError_t last_launch() { return hipGetLastError(); }
 
+// One batched bf16 GEMM launch over `per` tiles of each of `count` matrices.
+// A grid of 256-tiles runs in rounds of one workgroup per CU.  When the last
+// round is partial, its tiles run in a second launch as 128-tiles, four
+// workgroups per 256-tile (three on the diagonal of a symmetric output), so
+// the round costs about a third as long on an otherwise idle chip.  Tile size
+// changes no bit of the result.
+template <int TILE, int NPROD, typename Epi>
+static hipError_t gemm_launch(const uint16_t* Ah, const uint16_t* Al, int64_t lda, int64_t sA, const uint16_t* Bh,
+                              const uint16_t* Bl, int64_t ldb, int64_t sB, int64_t K, int tilesN, int upper, int per,
+                              int count, int cus, const Epi& epi, hipStream_t st) {
+  const int total = per * count;
+  int main = total;
+  if constexpr (TILE == 256) {
+    if (cus > 0 && total > cus) main = total - total % cus;
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<TILE, NPROD, Epi>), dim3(unsigned(main)), dim3(GemmGeom<TILE>::NT), 0, st,
+                     Ah, Al, lda, sA, Bh, Bl, ldb, sB, K, tilesN, upper, per, 0, 0, epi);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if constexpr (TILE == 256) {
+    if (main < total) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, NPROD, Epi>), dim3(unsigned(4 * (total - main))),
+                         dim3(GemmGeom<128>::NT), 0, st, Ah, Al, lda, sA, Bh, Bl, ldb, sB, K, tilesN, upper, per,
+                         main, 1, epi);
+      return hipGetLastError();
+    }
+  }
+  return hipSuccess;
+}
+
 // One NS step of the bf16 path: Gram, poly, apply.
 template <int TILE, typename PT>
 static hipError_t ns_step_bf16(const LargeArgs& g, hipStream_t st, int k, int cur, int last) {
-  using Geo = GemmGeom<TILE>;
   const LargeLayout& L = g.L;
   uint8_t* ws = (uint8_t*)g.ws;
   uint16_t* X = (uint16_t*)(ws + L.x);
@@ -690,25 +729,22 @@ static hipError_t ns_step_bf16(const LargeArgs& g, hipStream_t st, int k, int cu
   if (mp % TILE != 0 || np % TILE != 0) return hipErrorInvalidValue;
   const int Tm = int(mp / TILE), Tn = int(np / TILE);
   const unsigned up = unsigned(Tm * (Tm + 1) / 2);
-  const dim3 blk(Geo::NT);
   // Gram: upper tiles of [mp x mp], K = np
   EpiGramBf16 eg{A, H, Lo, scal, k == 0, mp};
-  hipLaunchKernelGGL((gemm_bf16_kernel<TILE, 1, EpiGramBf16>), dim3(up, g.count), blk, 0, st,
-                     (const uint16_t*)X, (const uint16_t*)nullptr, np, L.x_stride, (const uint16_t*)X,
-                     (const uint16_t*)nullptr, np, L.x_stride, np, Tm, 1, eg);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (hipError_t e = gemm_launch<TILE, 1>(X, nullptr, np, L.x_stride, X, nullptr, np, L.x_stride, np, Tm, 1, int(up),
+                                          g.count, g.cus, eg, st);
+      e != hipSuccess)
+    return e;
   // Poly: S = HH + HL + LH over upper tiles, K = mp
   EpiPolyBf16 ep{A, Poff, Pd, scal, k == 0, g.sc.a, g.sc.b, g.sc.c, mp, g.m};
-  hipLaunchKernelGGL((gemm_bf16_kernel<TILE, 3, EpiPolyBf16>), dim3(up, g.count), blk, 0, st,
-                     (const uint16_t*)H, (const uint16_t*)Lo, mp, L.a_stride, (const uint16_t*)H,
-                     (const uint16_t*)Lo, mp, L.a_stride, mp, Tm, 1, ep);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (hipError_t e = gemm_launch<TILE, 3>(H, Lo, mp, L.a_stride, H, Lo, mp, L.a_stride, mp, Tm, 1, int(up), g.count,
+                                          g.cus, ep, st);
+      e != hipSuccess)
+    return e;
   // Apply: X' = Poff Xt^T + diag(Pd) X, K = mp
   EpiApplyBf16<PT> ea{g.tab, g.sc, X, Xt[cur ^ 1], Pd, mp, np, g.m, g.n, last};
-  hipLaunchKernelGGL((gemm_bf16_kernel<TILE, 1, EpiApplyBf16<PT>>), dim3(unsigned(Tm * Tn), g.count), blk, 0,
-                     st, (const uint16_t*)Poff, (const uint16_t*)nullptr, mp, L.a_stride,
-                     (const uint16_t*)Xt[cur], (const uint16_t*)nullptr, mp, L.x_stride, mp, Tn, 0, ea);
-  return hipGetLastError();
+  return gemm_launch<TILE, 1>(Poff, nullptr, mp, L.a_stride, Xt[cur], nullptr, mp, L.x_stride, mp, Tn, 0, Tm * Tn,
+                              g.count, g.cus, ea, st);
 }
 
 template <typename PT, typename XT>

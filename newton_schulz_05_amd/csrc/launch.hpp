@@ -17,6 +17,7 @@ struct LargeArgs {
   int count;
   int64_t m, n, mp, np;
   int tile;          // bf16 GEMM tile (128 or 256)
+  int cus;           // compute units of the device (one 256-tile workgroup each)
   bool bf16;
 };
 

@@ -434,7 +434,8 @@ __device__ __forceinline__ void tile_coords(int t, int T, bool upper, int& ti, i
 // A, B row-major with k contiguous; all dims padded to the tile size.
 //
 // TILE x TILE output tile per block: 256 -> 8 waves (2 x 4) of 128 x 64,
-// 128 -> 4 waves (2 x 2) of 64 x 64; 32x32x16 MFMAs.  Operand tiles go from
+// 128 -> 4 waves (2 x 2) of 64 x 64, 64 -> 4 waves of 32 x 32 (only for the
+// partial last round of a 128-tile grid); 32x32x16 MFMAs.  Operand tiles go from
 // global memory straight into LDS (global_load_lds, 16 bytes a lane), two
 // stages, so no VGPRs are spent on staging.  Each 16-byte chunk of a row
 // sits at chunk index (c ^ g(row)) so that the fragment reads (32 rows x 2
@@ -455,7 +456,8 @@ struct GemmGeom {
   static constexpr int WM = 2;
   static constexpr int TMW = TILE / WM, TNW = TILE / WN;
   static constexpr int FM = TMW / 32, FN = TNW / 32;
-  static constexpr int MIN_BLOCKS = (TILE == 256) ? 1 : 2;
+  // co-resident workgroups per CU (LDS: 128 KB, 64 KB, 32 KB per workgroup)
+  static constexpr int PER_CU = (TILE == 256) ? 1 : (TILE == 128) ? 2 : 4;
 };
 
 // 16 bytes per lane from global memory into LDS; lane l writes lds_base + 16 l
@@ -470,7 +472,7 @@ __device__ __forceinline__ int chunk_swz(int row) {
 }
 
 template <int TILE, int NPROD, typename Epi>
-__global__ __launch_bounds__(TILE == 256 ? 512 : 256, TILE == 256 ? 1 : 2) void gemm_bf16_kernel(
+__global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void gemm_bf16_kernel(
     const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al, int64_t lda, int64_t sA,
     const uint16_t* __restrict__ Bh, const uint16_t* __restrict__ Bl, int64_t ldb, int64_t sB,
     int64_t K, int tilesN, int upper, int per, int base, int split, Epi epi) {
@@ -684,32 +686,27 @@ __global__ __launch_bounds__(256) void ns0_kernel(MatTable tab, StepScalars sc, 
 static hipError_t last_launch() { return hipGetLastError(); }
 
 // One batched bf16 GEMM launch over `per` tiles of each of `count` matrices.
-// A grid of 256-tiles runs in rounds of one workgroup per CU.  When the last
-// round is partial, its tiles run in a second launch as 128-tiles, four
-// workgroups per 256-tile (three on the diagonal of a symmetric output), so
-// the round costs about a third as long on an otherwise idle chip.  Tile size
+// A grid runs in rounds of PER_CU workgroups per CU.  When the last round is
+// partial, its tiles run in a second launch at half the tile size, four
+// workgroups per tile (three on the diagonal of a symmetric output), so that
+// round costs a fraction of a full one on an otherwise idle chip.  Tile size
 // changes no bit of the result.
 template <int TILE, int NPROD, typename Epi>
 static hipError_t gemm_launch(const uint16_t* Ah, const uint16_t* Al, int64_t lda, int64_t sA, const uint16_t* Bh,
                               const uint16_t* Bl, int64_t ldb, int64_t sB, int64_t K, int tilesN, int upper, int per,
                               int count, int cus, const Epi& epi, hipStream_t st) {
   const int total = per * count;
-  int main = total;
-  if constexpr (TILE == 256) {
-    if (cus > 0 && total > cus) main = total - total % cus;
-  }
+  const int round = cus * GemmGeom<TILE>::PER_CU;
+  const int main = (cus > 0 && total > round) ? total - total % round : total;
   hipLaunchKernelGGL((gemm_bf16_kernel<TILE, NPROD, Epi>), dim3(unsigned(main)), dim3(GemmGeom<TILE>::NT), 0, st,
                      Ah, Al, lda, sA, Bh, Bl, ldb, sB, K, tilesN, upper, per, 0, 0, epi);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  if constexpr (TILE == 256) {
-    if (main < total) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<128, NPROD, Epi>), dim3(unsigned(4 * (total - main))),
-                         dim3(GemmGeom<128>::NT), 0, st, Ah, Al, lda, sA, Bh, Bl, ldb, sB, K, tilesN, upper, per,
-                         main, 1, epi);
-      return hipGetLastError();
-    }
-  }
-  return hipSuccess;
+  if (main == total) return hipSuccess;
+  constexpr int SUB = TILE / 2;
+  hipLaunchKernelGGL((gemm_bf16_kernel<SUB, NPROD, Epi>), dim3(unsigned(4 * (total - main))),
+                     dim3(GemmGeom<SUB>::NT), 0, st, Ah, Al, lda, sA, Bh, Bl, ldb, sB, K, tilesN, upper, per, main, 1,
+                     epi);
+  return hipGetLastError();
 }
 
 // One NS step of the bf16 path: Gram, poly, apply.

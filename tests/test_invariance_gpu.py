@@ -169,3 +169,18 @@ def test_ranks_stepping_their_assigned_matrices_reproduce_the_full_step():
     for i in range(len(shapes)):
         assert torch.equal(p_split[i], full_p[i]), f"W[{i}]"
         assert torch.equal(m_split[i], full_m[i]), f"M[{i}]"
+
+
+@pytest.mark.parametrize("shapes", [[(2048, 1536)] * 8, [(1536, 2048)] * 5], ids=["gram_poly_split", "apply_split"])
+def test_partial_round_at_half_tile_is_bitwise_neutral(shapes):
+    """A 128-tile grid whose last round is partial runs that round as
+    64-tiles: eight transposed [2048, 1536] experts have 624 symmetric
+    128-tiles (Gram, poly) against 512 co-resident slots, five [1536, 2048]
+    have 960 apply tiles.  Each matrix stepped alone (one partial round, no
+    split) must give the same bits."""
+    params, grads = _draw(shapes, torch.bfloat16, 78)
+    pg, mg = _step(shapes, [p.clone() for p in params], grads, torch.bfloat16)
+    for i in (0, len(shapes) - 1):
+        p1, m1 = _step([shapes[i]], [params[i].clone()], [[grads[0][i]], [grads[1][i]]], torch.bfloat16)
+        assert torch.equal(p1[0], pg[i]), f"W[{i}] differs between the split and single-matrix grids"
+        assert torch.equal(m1[0], mg[i])

@@ -9,7 +9,8 @@
 //   gram (MFMA)       A = sc * X X^T on upper tiles (fp32, upper tiles only);
 //                     H = bf16(A) and L = bf16(A - H) for the split A^2,
 //                     mirrored to full matrices (they are GEMM operands)
-//   poly (MFMA)       S = H H + H L + L H  (A^2 to ~16 mantissa bits), then
+//   poly (MFMA)       S = H H + H L + L H  (A^2 to ~16 mantissa bits), or
+//                     S = H H in the steps before the last two when m >= 512;
 //                     P = ps * (a I + b A + c S); stores the off-diagonal part
 //                     in bf16 and the diagonal in fp32
 //   apply (MFMA)      X' = Poff Xt^T + diag(Pd) X; stores X' and X'^T in bf16,
@@ -276,9 +277,10 @@ struct NatStore {
 
 // Gram (bf16 path): A = sc2 * acc (upper tiles only: its only reader is the
 // poly epilogue at the same positions), plus its bf16 hi/lo split H, L, which
-// are GEMM operands and so are mirrored.
+// are GEMM operands and so are mirrored.  L is written only for steps whose
+// A^2 takes the split products (with_lo).
 struct EpiGramBf16 {
-  float* A; uint16_t* H; uint16_t* L; const float* scal; int use_scale; int64_t mp;
+  float* A; uint16_t* H; uint16_t* L; const float* scal; int use_scale; int with_lo; int64_t mp;
   static constexpr bool kCol = true;
   __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool diag) const {
     const float s2 = use_scale ? scal[z * 4 + 1] : 1.0f;
@@ -292,7 +294,7 @@ struct EpiGramBf16 {
     const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
     Seg<float>::store(A + o, k0, 16, v);
     Seg<uint16_t>::store(H + o, k0, 16, v);
-    Seg<uint16_t>::store(L + o, k0, 16, lo);
+    if (with_lo) Seg<uint16_t>::store(L + o, k0, 16, lo);
   }
   __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
     float lo[16];
@@ -301,7 +303,7 @@ struct EpiGramBf16 {
     const int k1 = diag ? clamp16(j - i0) : 16;  // diagonal tiles: mirror i < j only
     const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
     Seg<uint16_t>::store(H + o, 0, k1, v);
-    Seg<uint16_t>::store(L + o, 0, k1, lo);
+    if (with_lo) Seg<uint16_t>::store(L + o, 0, k1, lo);
   }
 };
 
@@ -709,6 +711,22 @@ static hipError_t gemm_launch(const uint16_t* Ah, const uint16_t* Al, int64_t ld
   return hipGetLastError();
 }
 
+// A^2 takes the split-bf16 products (H H + H L + L H, about 16 mantissa bits
+// of A) in every NS step for m < kPlainMinM, and otherwise only in the last
+// two steps, the earlier ones taking the single product H H.  NS pulls every
+// singular value towards its fixed band, which damps a perturbation of an
+// early step's P; the steps whose rounding of A shows in O are those after the
+// bulk of the normalised singular values (about 1/sqrt(m) at the start, times
+// up to a = 3.4445 per step) has reached the band.  In an emulation of this
+// recipe on Gaussian inputs with the quintic coefficients and 5 steps, a
+// single-product A^2 in steps 0-2 moved the relative Frobenius error of O by
+// under 0.5% of itself at 512^2, 1024^2 and 1024 x 3584 (6.89e-3 -> 6.92e-3 at
+// 512^2; inputs with singular values spread over 1e-1 .. 1e-4 the same), while
+// a single product in the last step alone raised it by 15-35%; at m = 33 .. 130
+// the third-last step already counts (5.6e-3 -> 8.4e-3 at 130 x 200).
+constexpr int kSplitSteps = 2;
+constexpr int64_t kPlainMinM = 512;
+
 // One NS step of the bf16 path: Gram, poly, apply.
 template <int TILE, typename PT>
 static hipError_t ns_step_bf16(const LargeArgs& g, hipStream_t st, int k, int cur, int last) {
@@ -726,16 +744,19 @@ static hipError_t ns_step_bf16(const LargeArgs& g, hipStream_t st, int k, int cu
   if (mp % TILE != 0 || np % TILE != 0) return hipErrorInvalidValue;
   const int Tm = int(mp / TILE), Tn = int(np / TILE);
   const unsigned up = unsigned(Tm * (Tm + 1) / 2);
+  const bool split = g.m < kPlainMinM || k >= g.sc.ns_steps - kSplitSteps;
   // Gram: upper tiles of [mp x mp], K = np
-  EpiGramBf16 eg{A, H, Lo, scal, k == 0, mp};
+  EpiGramBf16 eg{A, H, Lo, scal, k == 0, split ? 1 : 0, mp};
   if (hipError_t e = gemm_launch<TILE, 1>(X, nullptr, np, L.x_stride, X, nullptr, np, L.x_stride, np, Tm, 1, int(up),
                                           g.count, g.cus, eg, st);
       e != hipSuccess)
     return e;
-  // Poly: S = HH + HL + LH over upper tiles, K = mp
+  // Poly: S = HH + HL + LH (split steps) or S = HH over upper tiles, K = mp
   EpiPolyBf16 ep{A, Poff, Pd, scal, k == 0, g.sc.a, g.sc.b, g.sc.c, mp, g.m};
-  if (hipError_t e = gemm_launch<TILE, 3>(H, Lo, mp, L.a_stride, H, Lo, mp, L.a_stride, mp, Tm, 1, int(up), g.count,
-                                          g.cus, ep, st);
+  if (hipError_t e = split ? gemm_launch<TILE, 3>(H, Lo, mp, L.a_stride, H, Lo, mp, L.a_stride, mp, Tm, 1, int(up),
+                                                  g.count, g.cus, ep, st)
+                           : gemm_launch<TILE, 1>(H, nullptr, mp, L.a_stride, H, nullptr, mp, L.a_stride, mp, Tm, 1,
+                                                  int(up), g.count, g.cus, ep, st);
       e != hipSuccess)
     return e;
   // Apply: X' = Poff Xt^T + diag(Pd) X, K = mp

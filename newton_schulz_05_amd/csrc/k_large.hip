@@ -10,7 +10,7 @@
 //                     H = bf16(A) and L = bf16(A - H) for the split A^2,
 //                     mirrored to full matrices (they are GEMM operands)
 //   poly (MFMA)       S = H H + H L + L H  (A^2 to ~16 mantissa bits), or
-//                     S = H H in the steps before the last two when m >= 512;
+//                     S = H H in the first steps when m >= 512 (split_a2);
 //                     P = ps * (a I + b A + c S); stores the off-diagonal part
 //                     in bf16 and the diagonal in fp32
 //   apply (MFMA)      X' = Poff Xt^T + diag(Pd) X; stores X' and X'^T in bf16,
@@ -337,6 +337,81 @@ struct EpiPolyBf16 {
   __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
     const int k1 = diag ? clamp16(j - i0) : 16;
     Seg<uint16_t>::store(Poff + int64_t(z) * mp * mp + j * mp + i0, 0, k1, v);
+  }
+};
+
+// Paired steps, m x m products of commuting symmetric matrices (bf16 path):
+// C = acc + d[i] * S[i][j], with acc = Poff B^T from the GEMM, d the fp32
+// diagonal of the left factor and S the right factor in fp32 (upper tiles).
+// Gives T = P_k A_k and A_{k+1} = P_k T.  C is stored in fp32 over S (same
+// position, same thread: in place), and as bf16 hi (and lo when with_lo),
+// mirrored to full matrices since they are GEMM operands.
+struct EpiSymMul {
+  float* S; const float* d; uint16_t* H; uint16_t* L; int with_lo; int64_t mp;
+  static constexpr bool kCol = true;
+  __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool diag) const {
+    const int k0 = diag ? clamp16(i - j0) : 0;  // diagonal tiles: j >= i
+    const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
+    float sv[16] = {}, lo[16];
+    Seg<float>::load(S + o, k0, 16, sv);
+    const float di = d[int64_t(z) * mp + i];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v[k] = fmaf(di, sv[k], v[k]);
+      lo[k] = v[k] - bf2f(f2bf(v[k]));
+    }
+    Seg<float>::store(S + o, k0, 16, v);
+    Seg<uint16_t>::store(H + o, k0, 16, v);
+    if (with_lo) Seg<uint16_t>::store(L + o, k0, 16, lo);
+  }
+  __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
+    const int k1 = diag ? clamp16(j - i0) : 16;  // diagonal tiles: mirror i < j only
+    const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
+    Seg<uint16_t>::store(H + o, 0, k1, v);
+    if (with_lo) {
+      float lo[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
+      Seg<uint16_t>::store(L + o, 0, k1, lo);
+    }
+  }
+};
+
+// Paired steps: R = ps * P_{k+1} P_k with P = Poff + diag(Pd) for both
+// factors: acc = Poff1 Poff0^T from the GEMM, plus Pd1[i] Poff0[i][j] +
+// Poff1[i][j] Pd0[j] + [i == j] Pd1[i] Pd0[i].  Off-diagonal R in bf16
+// (mirrored), diagonal in fp32, the layout the apply takes.
+struct EpiPairR {
+  const uint16_t* Poff0; const float* Pd0; const uint16_t* Poff1; const float* Pd1;
+  uint16_t* Roff; float* Rd; const float* scal; int use_scale; int64_t mp;
+  static constexpr bool kCol = true;
+  __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool diag) const {
+    const float ps = use_scale ? scal[z * 4 + 0] : 1.0f;
+    const int k0 = diag ? clamp16(i - j0) : 0;
+    const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
+    float p0[16] = {}, p1[16] = {}, d0[16] = {}, rv[16];
+    Seg<uint16_t>::load(Poff0 + o, k0, 16, p0);
+    Seg<uint16_t>::load(Poff1 + o, k0, 16, p1);
+    Seg<float>::load(Pd0 + int64_t(z) * mp + j0, k0, 16, d0);
+    const float d1 = Pd1[int64_t(z) * mp + i];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      float r = fmaf(d1, p0[k], fmaf(p1[k], d0[k], v[k]));
+      if (i == j0 + k) {
+        r = ps * fmaf(d1, d0[k], r);
+        Rd[int64_t(z) * mp + i] = r;
+        rv[k] = 0.f;
+      } else {
+        r = ps * r;
+        rv[k] = r;
+      }
+      v[k] = r;
+    }
+    Seg<uint16_t>::store(Roff + o, k0, 16, rv);
+  }
+  __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
+    const int k1 = diag ? clamp16(j - i0) : 16;
+    Seg<uint16_t>::store(Roff + int64_t(z) * mp * mp + j * mp + i0, 0, k1, v);
   }
 };
 
@@ -711,21 +786,27 @@ static hipError_t gemm_launch(const uint16_t* Ah, const uint16_t* Al, int64_t ld
   return hipGetLastError();
 }
 
-// A^2 takes the split-bf16 products (H H + H L + L H, about 16 mantissa bits
-// of A) in every NS step for m < kPlainMinM, and otherwise only in the last
-// two steps, the earlier ones taking the single product H H.  NS pulls every
-// singular value towards its fixed band, which damps a perturbation of an
-// early step's P; the steps whose rounding of A shows in O are those after the
+// A^2 takes the single product H H in the first NS steps and the split-bf16
+// products (H H + H L + L H, about 16 mantissa bits of A) after them: for
+// m >= kPlainMinM the single product is taken in steps k < min(kPlainSteps,
+// ns_steps - 2), for smaller m never.  NS pulls every singular value towards
+// its fixed band and damps a perturbation of P on the way there; once the
 // bulk of the normalised singular values (about 1/sqrt(m) at the start, times
-// up to a = 3.4445 per step) has reached the band.  In an emulation of this
-// recipe on Gaussian inputs with the quintic coefficients and 5 steps, a
-// single-product A^2 in steps 0-2 moved the relative Frobenius error of O by
-// under 0.5% of itself at 512^2, 1024^2 and 1024 x 3584 (6.89e-3 -> 6.92e-3 at
-// 512^2; inputs with singular values spread over 1e-1 .. 1e-4 the same), while
-// a single product in the last step alone raised it by 15-35%; at m = 33 .. 130
-// the third-last step already counts (5.6e-3 -> 8.4e-3 at 130 x 200).
-constexpr int kSplitSteps = 2;
+// up to a = 3.4445 per step) has reached the band, the rounding of A shows in
+// O.  In an emulation of this recipe on Gaussian inputs with the quintic
+// coefficients, the single product in steps 0-2 moved the relative Frobenius
+// error of O by under 3% of itself at 512^2, 1024^2, 512 x 1024 and
+// 1024 x 3584 for 4 to 7 steps (6.89e-3 -> 6.92e-3 at 512^2 and 5 steps;
+// inputs with singular values spread over 1e-1 .. 1e-4 the same), while a
+// single product in step 3 (of 5 or 6) or in the last step raised it by
+// 15-240%; at m = 33 .. 130 step 2 already counts (5.6e-3 -> 8.4e-3 at
+// 130 x 200).
+constexpr int kPlainSteps = 3;
 constexpr int64_t kPlainMinM = 512;
+
+static inline bool split_a2(int64_t m, int k, int steps) {
+  return m < kPlainMinM || k >= std::min(kPlainSteps, steps - 2);
+}
 
 // One NS step of the bf16 path: Gram, poly, apply.
 template <int TILE, typename PT>
@@ -744,7 +825,7 @@ static hipError_t ns_step_bf16(const LargeArgs& g, hipStream_t st, int k, int cu
   if (mp % TILE != 0 || np % TILE != 0) return hipErrorInvalidValue;
   const int Tm = int(mp / TILE), Tn = int(np / TILE);
   const unsigned up = unsigned(Tm * (Tm + 1) / 2);
-  const bool split = g.m < kPlainMinM || k >= g.sc.ns_steps - kSplitSteps;
+  const bool split = split_a2(g.m, k, g.sc.ns_steps);
   // Gram: upper tiles of [mp x mp], K = np
   EpiGramBf16 eg{A, H, Lo, scal, k == 0, split ? 1 : 0, mp};
   if (hipError_t e = gemm_launch<TILE, 1>(X, nullptr, np, L.x_stride, X, nullptr, np, L.x_stride, np, Tm, 1, int(up),
@@ -763,6 +844,77 @@ static hipError_t ns_step_bf16(const LargeArgs& g, hipStream_t st, int k, int cu
   EpiApplyBf16<PT> ea{g.tab, g.sc, X, Xt[cur ^ 1], Pd, mp, np, g.m, g.n, last};
   return gemm_launch<TILE, 1>(Poff, nullptr, mp, L.a_stride, Xt[cur], nullptr, mp, L.x_stride, mp, Tn, 0, Tm * Tn,
                               g.count, g.cus, ea, st);
+}
+
+// Two NS steps k, k+1 of the bf16 path.  P, A and every product below are
+// polynomials in A_k, so they commute and the products are symmetric (upper
+// tiles, mirrored):
+//   Gram   A_k = sc X X^T                         (H, and L for a split A^2)
+//   poly   P_k = a I + b A_k + c A_k^2            -> Poff, Pd (no scale s)
+//   T      T = P_k A_k = Poff H^T + diag(Pd) A_k  -> fp32 in A's place, Th
+//   A'     A_{k+1} = P_k T = Poff Th^T + diag(Pd) T -> fp32 in A's place, H, L
+//   poly   P_{k+1} from A_{k+1}                   -> Poff2, Pd2
+//   R      R = ps P_{k+1} P_k                     -> off-diagonal in Th, Rd
+//   apply  X_{k+2} = Roff Xt^T + diag(Rd) X
+// A_{k+1} = X_{k+1} X_{k+1}^T in exact arithmetic (X_{k+1} = P_k X_k without
+// the scale s, which R carries on step 0), so this is the oracle's iteration
+// with one m x n product pair per two steps.  In an emulation of these
+// roundings (Gaussian inputs, quintic coefficients, 5 steps as a pair, a pair
+// and a single step) the relative Frobenius error of O fell next to single
+// steps on wide shapes (1024 x 3584: 4.2e-3 -> 3.6e-3; 512 x 4096: 4.7e-3 ->
+// 3.8e-3; 768 x 1024: unchanged), since X is rounded to bf16 half as often.
+template <int TILE, typename PT>
+static hipError_t ns_pair_bf16(const LargeArgs& g, hipStream_t st, int k, int cur, int last) {
+  const LargeLayout& L = g.L;
+  uint8_t* ws = (uint8_t*)g.ws;
+  uint16_t* X = (uint16_t*)(ws + L.x);
+  uint16_t* Xt[2] = {(uint16_t*)(ws + L.xt0), (uint16_t*)(ws + L.xt1)};
+  float* A = (float*)(ws + L.a);
+  float* scal = (float*)(ws + L.scal);
+  uint16_t* H = (uint16_t*)(ws + L.h);
+  uint16_t* Lo = (uint16_t*)(ws + L.l);
+  uint16_t* Poff = (uint16_t*)(ws + L.poff);
+  float* Pd = (float*)(ws + L.pdiag);
+  uint16_t* Th = (uint16_t*)(ws + L.th);
+  uint16_t* Poff2 = (uint16_t*)(ws + L.poff2);
+  float* Pd2 = (float*)(ws + L.pdiag2);
+  float* Rd = (float*)(ws + L.rdiag);
+  const int64_t mp = g.mp, np = g.np;
+  if (mp % TILE != 0 || np % TILE != 0 || !g.pair) return hipErrorInvalidValue;
+  const int Tm = int(mp / TILE), Tn = int(np / TILE);
+  const int up = Tm * (Tm + 1) / 2;
+  const int steps = g.sc.ns_steps;
+  const bool split0 = split_a2(g.m, k, steps);
+  const bool split1 = split_a2(g.m, k + 1, steps);
+  hipError_t e;
+  auto poly = [&](bool split, uint16_t* po, float* pd) {
+    EpiPolyBf16 ep{A, po, pd, scal, 0, g.sc.a, g.sc.b, g.sc.c, mp, g.m};
+    return split ? gemm_launch<TILE, 3>(H, Lo, mp, L.a_stride, H, Lo, mp, L.a_stride, mp, Tm, 1, up, g.count,
+                                        g.cus, ep, st)
+                 : gemm_launch<TILE, 1>(H, nullptr, mp, L.a_stride, H, nullptr, mp, L.a_stride, mp, Tm, 1, up,
+                                        g.count, g.cus, ep, st);
+  };
+  EpiGramBf16 eg{A, H, Lo, scal, k == 0, split0 ? 1 : 0, mp};
+  if ((e = gemm_launch<TILE, 1>(X, nullptr, np, L.x_stride, X, nullptr, np, L.x_stride, np, Tm, 1, up, g.count,
+                                g.cus, eg, st)) != hipSuccess)
+    return e;
+  if ((e = poly(split0, Poff, Pd)) != hipSuccess) return e;
+  EpiSymMul et{A, Pd, Th, nullptr, 0, mp};
+  if ((e = gemm_launch<TILE, 1>(Poff, nullptr, mp, L.a_stride, H, nullptr, mp, L.a_stride, mp, Tm, 1, up, g.count,
+                                g.cus, et, st)) != hipSuccess)
+    return e;
+  EpiSymMul ea1{A, Pd, H, Lo, split1 ? 1 : 0, mp};
+  if ((e = gemm_launch<TILE, 1>(Poff, nullptr, mp, L.a_stride, Th, nullptr, mp, L.a_stride, mp, Tm, 1, up, g.count,
+                                g.cus, ea1, st)) != hipSuccess)
+    return e;
+  if ((e = poly(split1, Poff2, Pd2)) != hipSuccess) return e;
+  EpiPairR er{Poff, Pd, Poff2, Pd2, Th, Rd, scal, k == 0, mp};
+  if ((e = gemm_launch<TILE, 1>(Poff2, nullptr, mp, L.a_stride, Poff, nullptr, mp, L.a_stride, mp, Tm, 1, up,
+                                g.count, g.cus, er, st)) != hipSuccess)
+    return e;
+  EpiApplyBf16<PT> eap{g.tab, g.sc, X, Xt[cur ^ 1], Rd, mp, np, g.m, g.n, last};
+  return gemm_launch<TILE, 1>(Th, nullptr, mp, L.a_stride, Xt[cur], nullptr, mp, L.x_stride, mp, Tn, 0, Tm * Tn,
+                              g.count, g.cus, eap, st);
 }
 
 template <typename PT, typename XT>
@@ -798,6 +950,15 @@ static hipError_t run_large_t(const LargeArgs& g, hipStream_t st) {
   for (int k = 0; k < steps; ++k) {
     const int last = (k == steps - 1);
     if constexpr (sizeof(XT) == 2) {
+      if (g.pair && k + 1 < steps) {
+        const int last2 = (k + 2 == steps);
+        const hipError_t e = (g.tile == 256) ? ns_pair_bf16<256, PT>(g, st, k, cur, last2)
+                                             : ns_pair_bf16<128, PT>(g, st, k, cur, last2);
+        if (e != hipSuccess) return e;
+        ++k;  // the pair took steps k and k + 1
+        cur ^= 1;
+        continue;
+      }
       const hipError_t e = (g.tile == 256) ? ns_step_bf16<256, PT>(g, st, k, cur, last)
                                            : ns_step_bf16<128, PT>(g, st, k, cur, last);
       if (e != hipSuccess) return e;

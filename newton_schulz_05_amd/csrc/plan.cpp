@@ -55,10 +55,25 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
     L.poff = take(size_t(count) * size_t(mp) * size_t(mp) * 4);  // full fp32 P
   }
   L.pdiag = take(size_t(count) * size_t(mp) * 4);
+  if (g.pair) {
+    L.th = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+    L.poff2 = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+    L.pdiag2 = take(size_t(count) * size_t(mp) * 4);
+    L.rdiag = take(size_t(count) * size_t(mp) * 4);
+  }
   L.normpart = take(size_t(count) * size_t(L.tiles) * 4);
   L.scal = take(size_t(count) * 4 * 4);
   L.bytes = off;
   return L;
+}
+
+bool mfma_pair(int64_t m, int64_t n) {
+  // Only where the products of the pair have been shown to keep O as
+  // accurate as the single steps (m >= 512, wide shapes), and where the
+  // saving outweighs the extra launch and the m x m epilogue traffic: at
+  // n = 1.33 m (8 x [1536, 2048]) pairs measured 15% slower, at n = 3.5 m
+  // ([8192, 28672], [4096, 14336]) 20-23% faster.
+  return m >= 512 && n >= 2 * m;
 }
 
 double ns_cost(int64_t rows, int64_t cols) {
@@ -175,6 +190,7 @@ muon_status build_plan(const muon_shape* shapes, int32_t n_params, muon_dtype pa
       g.chunks = split_even(count, cap);
     } else {
       g.tile = (g.path == PATH_MFMA) ? mfma_tile(g.m, g.n, count) : int32_t(kF32Tile);
+      g.pair = (g.path == PATH_MFMA) && mfma_pair(g.m, g.n);
       const int64_t t = g.tile;
       g.mp = round_up(g.m, t);
       g.np = round_up(g.n, t);

@@ -231,8 +231,10 @@ def executed_flops(wl) -> float:
     their upper tiles only; true m and n, padding not counted).  Mirrors the
     library's schedule: A^2 as one product in NS steps k < min(3, steps - 2)
     when m >= 512, as three split products otherwise; for m >= 512 and
-    n >= 2 m, steps taken in pairs (Gram m^2 n, then the m x m products
-    A^2, T = P A, A' = P T, A'^2, R = P' P, and one apply 2 m^2 n)."""
+    n >= 2 m, steps taken in groups (the first min(4, steps - 1), then pairs,
+    then a single step), each with one Gram m^2 n, per step the m x m products
+    A^2 and, after the group's first step, T = P A, A' = P T and R = P R, and
+    one apply 2 m^2 n."""
     N = wl.ns_steps
     tot = 0.0
     for s in wl.shapes:
@@ -242,16 +244,18 @@ def executed_flops(wl) -> float:
         if m <= 32:
             tot += b * (3.0 * m * m * n + m ** 3) * N
             continue
-        split = lambda k: m < 512 or k >= min(3, N - 2)  # noqa: E731
-        pair = m >= 512 and n >= 2 * m
+        a2 = lambda k: (1 if (m >= 512 and k < min(3, N - 2)) else 3) * m ** 3  # noqa: E731
+        grouped = m >= 512 and n >= 2 * m
         f, k = 0.0, 0
         while k < N:
-            if pair and k + 1 < N:
-                f += 3 * m * m * n + (3 if split(k) else 1) * m ** 3 + 3 * m ** 3 + (3 if split(k + 1) else 1) * m ** 3
-                k += 2
+            if not grouped:
+                G = 1
+            elif k == 0:
+                G = N if N <= 2 else min(4, N - 1)
             else:
-                f += 3 * m * m * n + (3 if split(k) else 1) * m ** 3
-                k += 1
+                G = 2 if N - k >= 2 else 1
+            f += 3 * m * m * n + sum(a2(k + j) for j in range(G)) + 3 * (G - 1) * m ** 3
+            k += G
         tot += b * f
     return tot
 

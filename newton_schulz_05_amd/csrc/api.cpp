@@ -168,7 +168,7 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         a.np = grp.np;
         a.tile = grp.tile;
         a.bf16 = (grp.path == PATH_MFMA);
-        a.pair = grp.pair;
+        a.grouped = grp.grouped;
         if (muon_status s = device_cus(&a.cus); s != MUON_OK) return s;
         e = run_large(a, st);
       }

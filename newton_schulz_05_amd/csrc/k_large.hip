@@ -340,10 +340,10 @@ struct EpiPolyBf16 {
   }
 };
 
-// Paired steps, m x m products of commuting symmetric matrices (bf16 path):
+// Grouped steps, m x m products of commuting symmetric matrices (bf16 path):
 // C = acc + d[i] * S[i][j], with acc = Poff B^T from the GEMM, d the fp32
 // diagonal of the left factor and S the right factor in fp32 (upper tiles).
-// Gives T = P_k A_k and A_{k+1} = P_k T.  C is stored in fp32 over S (same
+// Gives T = P_j A_j and A_{j+1} = P_j T.  C is stored in fp32 over S (same
 // position, same thread: in place), and as bf16 hi (and lo when with_lo),
 // mirrored to full matrices since they are GEMM operands.
 struct EpiSymMul {
@@ -377,10 +377,11 @@ struct EpiSymMul {
   }
 };
 
-// Paired steps: R = ps * P_{k+1} P_k with P = Poff + diag(Pd) for both
-// factors: acc = Poff1 Poff0^T from the GEMM, plus Pd1[i] Poff0[i][j] +
+// Grouped steps: R = ps * F1 F0 for two commuting symmetric factors stored as
+// off-diagonal bf16 plus fp32 diagonal (F0 = Poff0 + diag(Pd0), the same for
+// F1): acc = Poff1 Poff0^T from the GEMM, plus Pd1[i] Poff0[i][j] +
 // Poff1[i][j] Pd0[j] + [i == j] Pd1[i] Pd0[i].  Off-diagonal R in bf16
-// (mirrored), diagonal in fp32, the layout the apply takes.
+// (mirrored), diagonal in fp32, the layout the apply and the next R take.
 struct EpiPairR {
   const uint16_t* Poff0; const float* Pd0; const uint16_t* Poff1; const float* Pd1;
   uint16_t* Roff; float* Rd; const float* scal; int use_scale; int64_t mp;
@@ -846,25 +847,34 @@ static hipError_t ns_step_bf16(const LargeArgs& g, hipStream_t st, int k, int cu
                               g.count, g.cus, ea, st);
 }
 
-// Two NS steps k, k+1 of the bf16 path.  P, A and every product below are
-// polynomials in A_k, so they commute and the products are symmetric (upper
-// tiles, mirrored):
-//   Gram   A_k = sc X X^T                         (H, and L for a split A^2)
-//   poly   P_k = a I + b A_k + c A_k^2            -> Poff, Pd (no scale s)
-//   T      T = P_k A_k = Poff H^T + diag(Pd) A_k  -> fp32 in A's place, Th
-//   A'     A_{k+1} = P_k T = Poff Th^T + diag(Pd) T -> fp32 in A's place, H, L
-//   poly   P_{k+1} from A_{k+1}                   -> Poff2, Pd2
-//   R      R = ps P_{k+1} P_k                     -> off-diagonal in Th, Rd
-//   apply  X_{k+2} = Roff Xt^T + diag(Rd) X
-// A_{k+1} = X_{k+1} X_{k+1}^T in exact arithmetic (X_{k+1} = P_k X_k without
-// the scale s, which R carries on step 0), so this is the oracle's iteration
-// with one m x n product pair per two steps.  In an emulation of these
-// roundings (Gaussian inputs, quintic coefficients, 5 steps as a pair, a pair
-// and a single step) the relative Frobenius error of O fell next to single
-// steps on wide shapes (1024 x 3584: 4.2e-3 -> 3.6e-3; 512 x 4096: 4.7e-3 ->
-// 3.8e-3; 768 x 1024: unchanged), since X is rounded to bf16 half as often.
+// Steps of a group (bf16 path, wide groups): G >= 2 consecutive NS steps
+// k .. k+G-1 with one Gram and one apply.  Every P_j, A_j and product below is
+// a polynomial in A_k, so they commute and the products are symmetric (upper
+// tiles, mirrored).  For j = 0 .. G-1:
+//   j = 0   Gram  A_0 = sc X X^T                  -> A fp32 (upper), H (+ L)
+//           poly  P_0 = a I + b A_0 + c A_0^2     -> Pb[0] (no scale s)
+//   j >= 1  T     T = P_{j-1} A_{j-1}             -> fp32 over A, Th
+//           A'    A_j = P_{j-1} T                 -> fp32 over A, H (+ L)
+//           poly  P_j from A_j                    -> Pb[j % 2]
+//           R     R_j = P_j R_{j-1}, R_0 = s P_0  -> Rb[j % 2] (off-diagonal
+//                 bf16, diagonal fp32; s only when k = 0)
+//   apply   X_{k+G} = Roff Xt^T + diag(Rd) X, R = R_{G-1}
+// A_j = X_{k+j} X_{k+j}^T in exact arithmetic, so this is the oracle's
+// iteration with one m x n product pair per group.
+//
+// Which steps are grouped (group_len): the first min(4, N - 1) steps of N
+// form one group, and the rest go in pairs with a single step last when odd
+// (N = 5: 4 + 1; 6: 4 + 2; 7: 4 + 2 + 1; 2: one pair).  In an emulation of
+// these roundings (quintic coefficients) this order was the most accurate of
+// those tried: early steps, whose normalised singular values are small and
+// whose P is near a I, lose nothing in the m x m space, while the last steps
+// need A from a fresh Gram of X.  At 1024 x 3584 with 5 steps the relative
+// Frobenius error of O was 4.2e-3 for single steps and 3.2e-3 grouped on
+// Gaussian inputs, 1.9e-2 and 6.4e-3 with singular values spread over
+// [1e-2, 1], 3.0e-2 and 8.1e-3 over [1e-3, 1]; one group of all 5 steps gave
+// 2.7e-3, 3.0e-2 and 4.7e-2.
 template <int TILE, typename PT>
-static hipError_t ns_pair_bf16(const LargeArgs& g, hipStream_t st, int k, int cur, int last) {
+static hipError_t ns_group_bf16(const LargeArgs& g, hipStream_t st, int k, int G, int cur, int last) {
   const LargeLayout& L = g.L;
   uint8_t* ws = (uint8_t*)g.ws;
   uint16_t* X = (uint16_t*)(ws + L.x);
@@ -873,48 +883,60 @@ static hipError_t ns_pair_bf16(const LargeArgs& g, hipStream_t st, int k, int cu
   float* scal = (float*)(ws + L.scal);
   uint16_t* H = (uint16_t*)(ws + L.h);
   uint16_t* Lo = (uint16_t*)(ws + L.l);
-  uint16_t* Poff = (uint16_t*)(ws + L.poff);
-  float* Pd = (float*)(ws + L.pdiag);
   uint16_t* Th = (uint16_t*)(ws + L.th);
-  uint16_t* Poff2 = (uint16_t*)(ws + L.poff2);
-  float* Pd2 = (float*)(ws + L.pdiag2);
-  float* Rd = (float*)(ws + L.rdiag);
+  uint16_t* Pb[2] = {(uint16_t*)(ws + L.poff), (uint16_t*)(ws + L.poff2)};
+  float* Pdb[2] = {(float*)(ws + L.pdiag), (float*)(ws + L.pdiag2)};
+  uint16_t* Rb[2] = {(uint16_t*)(ws + L.roff0), (uint16_t*)(ws + L.roff1)};
+  float* Rdb[2] = {(float*)(ws + L.rdiag0), (float*)(ws + L.rdiag1)};
   const int64_t mp = g.mp, np = g.np;
-  if (mp % TILE != 0 || np % TILE != 0 || !g.pair) return hipErrorInvalidValue;
+  if (mp % TILE != 0 || np % TILE != 0 || !g.grouped || G < 2) return hipErrorInvalidValue;
   const int Tm = int(mp / TILE), Tn = int(np / TILE);
   const int up = Tm * (Tm + 1) / 2;
   const int steps = g.sc.ns_steps;
-  const bool split0 = split_a2(g.m, k, steps);
-  const bool split1 = split_a2(g.m, k + 1, steps);
   hipError_t e;
-  auto poly = [&](bool split, uint16_t* po, float* pd) {
-    EpiPolyBf16 ep{A, po, pd, scal, 0, g.sc.a, g.sc.b, g.sc.c, mp, g.m};
+  auto poly = [&](int j) {
+    const bool split = split_a2(g.m, k + j, steps);
+    EpiPolyBf16 ep{A, Pb[j & 1], Pdb[j & 1], scal, 0, g.sc.a, g.sc.b, g.sc.c, mp, g.m};
     return split ? gemm_launch<TILE, 3>(H, Lo, mp, L.a_stride, H, Lo, mp, L.a_stride, mp, Tm, 1, up, g.count,
                                         g.cus, ep, st)
                  : gemm_launch<TILE, 1>(H, nullptr, mp, L.a_stride, H, nullptr, mp, L.a_stride, mp, Tm, 1, up,
                                         g.count, g.cus, ep, st);
   };
-  EpiGramBf16 eg{A, H, Lo, scal, k == 0, split0 ? 1 : 0, mp};
+  EpiGramBf16 eg{A, H, Lo, scal, k == 0, split_a2(g.m, k, steps) ? 1 : 0, mp};
   if ((e = gemm_launch<TILE, 1>(X, nullptr, np, L.x_stride, X, nullptr, np, L.x_stride, np, Tm, 1, up, g.count,
                                 g.cus, eg, st)) != hipSuccess)
     return e;
-  if ((e = poly(split0, Poff, Pd)) != hipSuccess) return e;
-  EpiSymMul et{A, Pd, Th, nullptr, 0, mp};
-  if ((e = gemm_launch<TILE, 1>(Poff, nullptr, mp, L.a_stride, H, nullptr, mp, L.a_stride, mp, Tm, 1, up, g.count,
-                                g.cus, et, st)) != hipSuccess)
-    return e;
-  EpiSymMul ea1{A, Pd, H, Lo, split1 ? 1 : 0, mp};
-  if ((e = gemm_launch<TILE, 1>(Poff, nullptr, mp, L.a_stride, Th, nullptr, mp, L.a_stride, mp, Tm, 1, up, g.count,
-                                g.cus, ea1, st)) != hipSuccess)
-    return e;
-  if ((e = poly(split1, Poff2, Pd2)) != hipSuccess) return e;
-  EpiPairR er{Poff, Pd, Poff2, Pd2, Th, Rd, scal, k == 0, mp};
-  if ((e = gemm_launch<TILE, 1>(Poff2, nullptr, mp, L.a_stride, Poff, nullptr, mp, L.a_stride, mp, Tm, 1, up,
-                                g.count, g.cus, er, st)) != hipSuccess)
-    return e;
-  EpiApplyBf16<PT> eap{g.tab, g.sc, X, Xt[cur ^ 1], Rd, mp, np, g.m, g.n, last};
-  return gemm_launch<TILE, 1>(Th, nullptr, mp, L.a_stride, Xt[cur], nullptr, mp, L.x_stride, mp, Tn, 0, Tm * Tn,
-                              g.count, g.cus, eap, st);
+  if ((e = poly(0)) != hipSuccess) return e;
+  for (int j = 1; j < G; ++j) {
+    const int pp = (j - 1) & 1;  // P_{j-1}
+    EpiSymMul et{A, Pdb[pp], Th, nullptr, 0, mp};
+    if ((e = gemm_launch<TILE, 1>(Pb[pp], nullptr, mp, L.a_stride, H, nullptr, mp, L.a_stride, mp, Tm, 1, up,
+                                  g.count, g.cus, et, st)) != hipSuccess)
+      return e;
+    EpiSymMul ea{A, Pdb[pp], H, Lo, split_a2(g.m, k + j, steps) ? 1 : 0, mp};
+    if ((e = gemm_launch<TILE, 1>(Pb[pp], nullptr, mp, L.a_stride, Th, nullptr, mp, L.a_stride, mp, Tm, 1, up,
+                                  g.count, g.cus, ea, st)) != hipSuccess)
+      return e;
+    if ((e = poly(j)) != hipSuccess) return e;
+    // R_j = P_j R_{j-1}; R_0 = s P_0 is P_0 itself with the scale applied here
+    const uint16_t* r0 = (j == 1) ? Pb[0] : Rb[(j - 1) & 1];
+    const float* rd0 = (j == 1) ? Pdb[0] : Rdb[(j - 1) & 1];
+    EpiPairR er{r0, rd0, Pb[j & 1], Pdb[j & 1], Rb[j & 1], Rdb[j & 1], scal, (k == 0 && j == 1) ? 1 : 0, mp};
+    if ((e = gemm_launch<TILE, 1>(Pb[j & 1], nullptr, mp, L.a_stride, r0, nullptr, mp, L.a_stride, mp, Tm, 1, up,
+                                  g.count, g.cus, er, st)) != hipSuccess)
+      return e;
+  }
+  EpiApplyBf16<PT> eap{g.tab, g.sc, X, Xt[cur ^ 1], Rdb[(G - 1) & 1], mp, np, g.m, g.n, last};
+  return gemm_launch<TILE, 1>(Rb[(G - 1) & 1], nullptr, mp, L.a_stride, Xt[cur], nullptr, mp, L.x_stride, mp, Tn, 0,
+                              Tm * Tn, g.count, g.cus, eap, st);
+}
+
+// Steps taken together from step k of `steps` (grouped path): the first
+// min(4, steps - 1) (all of them when steps <= 2), then pairs, then a
+// single step when the count left is odd.
+static inline int group_len(int k, int steps) {
+  if (k == 0) return steps <= 2 ? steps : std::min(4, steps - 1);
+  return (steps - k >= 2) ? 2 : 1;
 }
 
 template <typename PT, typename XT>
@@ -950,12 +972,13 @@ static hipError_t run_large_t(const LargeArgs& g, hipStream_t st) {
   for (int k = 0; k < steps; ++k) {
     const int last = (k == steps - 1);
     if constexpr (sizeof(XT) == 2) {
-      if (g.pair && k + 1 < steps) {
-        const int last2 = (k + 2 == steps);
-        const hipError_t e = (g.tile == 256) ? ns_pair_bf16<256, PT>(g, st, k, cur, last2)
-                                             : ns_pair_bf16<128, PT>(g, st, k, cur, last2);
+      const int G = g.grouped ? group_len(k, steps) : 1;
+      if (G >= 2) {
+        const int lastG = (k + G == steps);
+        const hipError_t e = (g.tile == 256) ? ns_group_bf16<256, PT>(g, st, k, G, cur, lastG)
+                                             : ns_group_bf16<128, PT>(g, st, k, G, cur, lastG);
         if (e != hipSuccess) return e;
-        ++k;  // the pair took steps k and k + 1
+        k += G - 1;  // the group took steps k .. k + G - 1
         cur ^= 1;
         continue;
       }

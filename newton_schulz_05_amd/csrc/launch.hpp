@@ -19,7 +19,7 @@ struct LargeArgs {
   int tile;          // bf16 GEMM tile (128 or 256)
   int cus;           // compute units of the device (one 256-tile workgroup each)
   bool bf16;
-  bool pair;         // NS steps two at a time (bf16 path)
+  bool grouped;      // NS steps taken in groups (bf16 path)
 };
 
 // u32 indices, in the workspace's sync region, of the skinny path's timeout

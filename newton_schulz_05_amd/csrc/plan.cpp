@@ -55,11 +55,14 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
     L.poff = take(size_t(count) * size_t(mp) * size_t(mp) * 4);  // full fp32 P
   }
   L.pdiag = take(size_t(count) * size_t(mp) * 4);
-  if (g.pair) {
+  if (g.grouped) {
     L.th = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
     L.poff2 = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
     L.pdiag2 = take(size_t(count) * size_t(mp) * 4);
-    L.rdiag = take(size_t(count) * size_t(mp) * 4);
+    L.roff0 = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+    L.roff1 = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+    L.rdiag0 = take(size_t(count) * size_t(mp) * 4);
+    L.rdiag1 = take(size_t(count) * size_t(mp) * 4);
   }
   L.normpart = take(size_t(count) * size_t(L.tiles) * 4);
   L.scal = take(size_t(count) * 4 * 4);
@@ -67,11 +70,11 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
   return L;
 }
 
-bool mfma_pair(int64_t m, int64_t n) {
-  // Only where the products of the pair have been shown to keep O as
-  // accurate as the single steps (m >= 512, wide shapes), and where the
-  // saving outweighs the extra launch and the m x m epilogue traffic: at
-  // n = 1.33 m (8 x [1536, 2048]) pairs measured 15% slower, at n = 3.5 m
+bool mfma_grouped(int64_t m, int64_t n) {
+  // Only where grouped steps have been shown to keep O as accurate as single
+  // steps (m >= 512, wide shapes), and where the saving outweighs the extra
+  // launches and the m x m epilogue traffic: pairs at n = 1.33 m
+  // (8 x [1536, 2048]) measured 15% slower than single steps, at n = 3.5 m
   // ([8192, 28672], [4096, 14336]) 20-23% faster.
   return m >= 512 && n >= 2 * m;
 }
@@ -190,7 +193,7 @@ muon_status build_plan(const muon_shape* shapes, int32_t n_params, muon_dtype pa
       g.chunks = split_even(count, cap);
     } else {
       g.tile = (g.path == PATH_MFMA) ? mfma_tile(g.m, g.n, count) : int32_t(kF32Tile);
-      g.pair = (g.path == PATH_MFMA) && mfma_pair(g.m, g.n);
+      g.grouped = (g.path == PATH_MFMA) && mfma_grouped(g.m, g.n);
       const int64_t t = g.tile;
       g.mp = round_up(g.m, t);
       g.np = round_up(g.n, t);

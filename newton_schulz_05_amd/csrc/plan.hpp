@@ -55,7 +55,7 @@ struct Chunk {
 // MFMA and fp32 paths.  Per-matrix strides are in elements of the buffer type.
 struct LargeLayout {
   size_t x, xt0, xt1, a, h, l, poff, pdiag, normpart, scal;
-  size_t th, poff2, pdiag2, rdiag;    // paired NS steps only (Group::pair), else 0
+  size_t th, poff2, pdiag2, roff0, roff1, rdiag0, rdiag1;  // grouped steps only, else 0
   int64_t x_stride, a_stride, tiles;  // elements per matrix (X / A) and momentum tiles per matrix
   size_t bytes;                       // total bytes of the chunk region
 };
@@ -68,7 +68,7 @@ struct Group {
   std::vector<Chunk> chunks;
   int64_t mp = 0, np = 0;      // padded dims (MFMA / fp32 paths)
   int32_t tile = 0;            // MFMA path: GEMM output tile (128 or 256)
-  bool pair = false;           // MFMA path: NS steps taken two at a time (mfma_pair)
+  bool grouped = false;        // MFMA path: NS steps taken in groups (mfma_grouped)
   int32_t slabs = 0;           // skinny: column slabs per matrix
   int64_t slab_w = 0;          // skinny: columns per slab (multiple of 32)
   int32_t max_chunk = 0;       // largest chunk of this group
@@ -106,12 +106,13 @@ void assign_greedy(const Plan& P, int32_t n_ranks, std::vector<int32_t>* owner, 
 // GEMM tile of an MFMA-path group of `count` matrices of wide shape [m, n].
 int32_t mfma_tile(int64_t m, int64_t n, int64_t count);
 
-// Whether an MFMA-path group of wide shape [m, n] takes its NS steps two at a
-// time: X_{k+2} = (P_{k+1} P_k) X_k, with A_{k+1} = P_k A_k P_k formed in the
-// m x m space instead of as the Gram of X_{k+1}.  Two steps then cost
-// 3 m^2 n + 5 m^3 flops instead of 6 m^2 n + 2 m^3 (single-product A^2),
-// a saving once n > m; taken for m >= 512 and n >= 2 m.
-bool mfma_pair(int64_t m, int64_t n);
+// Whether an MFMA-path group of wide shape [m, n] takes its NS steps in
+// groups: steps k .. k+G-1 with one Gram of X_k and one apply of
+// R = P_{k+G-1} ... P_k, the A_j in between formed in the m x m space
+// (A_{j+1} = P_j A_j P_j).  A group of G steps costs 3 m^2 n + (4 G - 3) m^3
+// flops (single-product A^2) instead of G (3 m^2 n + m^3), a saving once
+// n > m; taken for m >= 512 and n >= 2 m.
+bool mfma_grouped(int64_t m, int64_t n);
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }

@@ -123,20 +123,21 @@ def test_few_ns_steps(ns_steps, dt):
 
 
 @pytest.mark.parametrize("ns_steps", [1, 2, 3, 4, 5, 6, 7])
-def test_paired_steps(ns_steps):
-    """Wide groups with m >= 512 and n >= 2 m take their NS steps in pairs
-    (A_{k+1} formed in the m x m space, one apply per pair), with a single
-    step left over for an odd count; the square group beside them takes
-    single steps (which also covers the single-product A^2 of the first
-    steps at every count).  From one step (no pair) to three pairs, with
-    ragged padding (600 x 1300 pads to 640 x 1408) and a tall member.
-    The square member sits out the 7-step case: the bf16 recipe's own error
-    on square shapes grows with the step count and reaches ~9.5e-3 at 7 steps
-    in a CPU emulation, with or without the single-product A^2, too close to
-    the 1e-2 bar (which is set for 5 steps)."""
+def test_grouped_steps(ns_steps):
+    """Wide groups with m >= 512 and n >= 2 m take their NS steps in groups
+    (one Gram and one apply per group, the A in between formed in the m x m
+    space): the first min(4, steps - 1) steps, then pairs, then a single step
+    (1: one step; 2: a pair; 3: 2 + 1; 5: 4 + 1; 6: 4 + 2; 7: 4 + 2 + 1).  The
+    square member takes single steps (which also covers the single-product
+    A^2 of the first steps at every count).  Ragged padding (600 x 1300 pads
+    to 640 x 1408) and a tall member.  The square member sits out the 7-step
+    case: the bf16 recipe's own error on square shapes grows with the step
+    count and reaches ~9.5e-3 at 7 steps in a CPU emulation, with or without
+    the single-product A^2, too close to the 1e-2 bar (which is set for 5
+    steps)."""
     shapes = [(512, 1024), (1300, 600)] + ([(512, 512)] if ns_steps <= 6 else [])
     wl = WL.custom(shapes, dtype=torch.bfloat16, g_std=1e-3, ns_steps=ns_steps, number=91)
-    _banner(f"paired steps, ns_steps={ns_steps}")
+    _banner(f"grouped steps, ns_steps={ns_steps}")
     res = run_and_compare(wl, steps=2) + ns_and_compare(wl)
     _banner(f"ns_steps={ns_steps}: worst O relF {max(r for r, _ in res):.3e}")
 

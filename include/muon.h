@@ -18,6 +18,20 @@
  *     X   <- a*X + (b*A + c*A^2)*X  with A = X*X^T, ns_steps times
  *     O    = X (transposed back if the parameter is tall)
  *     W   <- W - lr*(scale*O + wd*W)
+ * How the NS iteration is evaluated (the result is that iteration's, up to
+ * rounding):
+ *   - bf16, min(M, N) <= 32: X = Q_k X0 with Q_k a polynomial in X0 X0^T,
+ *     run in fp32 on the small m x m matrices (one Gram of X0 per call);
+ *   - bf16, larger: X stored in bf16, products on bf16 MFMA with fp32
+ *     accumulation; A^2 from a hi/lo bf16 split of A except in the first
+ *     min(3, ns_steps - 2) steps when min(M, N) >= 512; for wide shapes
+ *     (max >= 2 min >= 1024) the first min(4, ns_steps - 1) steps share one
+ *     Gram and one product with X (A_{k+1} = P_k A_k P_k in the m x m space),
+ *     then steps go in pairs;
+ *   - fp32: the same sequence as the bf16 path for larger matrices but with
+ *     fp32 FMA arithmetic throughout, one step at a time.
+ * On Gaussian inputs the bf16 O is within about 1e-2 relative Frobenius of
+ * the exact iteration for 5 quintic steps; the fp32 O within about 1e-5.
  *
  * Conventions for every entry point:
  *   - Device buffers (params, grads, momenta, outputs, workspace) belong to

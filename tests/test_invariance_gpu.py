@@ -171,13 +171,16 @@ def test_ranks_stepping_their_assigned_matrices_reproduce_the_full_step():
         assert torch.equal(m_split[i], full_m[i]), f"M[{i}]"
 
 
-@pytest.mark.parametrize("shapes", [[(2048, 1536)] * 8, [(1536, 2048)] * 5], ids=["gram_poly_split", "apply_split"])
-def test_partial_round_at_half_tile_is_bitwise_neutral(shapes):
-    """A 128-tile grid whose last round is partial runs that round as
-    64-tiles: eight transposed [2048, 1536] experts have 624 symmetric
-    128-tiles (Gram, poly) against 512 co-resident slots, five [1536, 2048]
-    have 960 apply tiles.  Each matrix stepped alone (one partial round, no
-    split) must give the same bits."""
+@pytest.mark.parametrize("shapes", [[(2048, 1536)] * 8, [(1536, 2048)] * 5, [(4096, 8192)] * 2],
+                         ids=["gram_poly_split", "apply_split", "symmetric_256_split"])
+def test_partial_round_at_smaller_tile_is_bitwise_neutral(shapes):
+    """A grid whose last round is partial runs that round at half the tile
+    size: eight transposed [2048, 1536] experts have 624 symmetric 128-tiles
+    (Gram, poly) against 512 co-resident slots, five [1536, 2048] have 960
+    apply tiles, and two [4096, 8192] (256-tiles, grouped NS steps) have 272
+    symmetric 256-tiles against 256 slots for the Gram and every m x m
+    product.  Each matrix stepped alone (no split; 128-tiles for a single
+    [4096, 8192]) must give the same bits."""
     params, grads = _draw(shapes, torch.bfloat16, 78)
     pg, mg = _step(shapes, [p.clone() for p in params], grads, torch.bfloat16)
     for i in (0, len(shapes) - 1):

@@ -1,7 +1,8 @@
 """Seeded random parameter sets against the fp64 oracle (two steps, the
 step's own O, and muon_ns).  Each set mixes shapes that exercise different
 kernels and edge cases: skinny (m <= 32; KS 6 and 8), MFMA groups with both
-GEMM tiles, tall members, expert slabs and ragged sizes.  The shapes come from
+GEMM tiles, single and grouped NS steps at m >= 512, tall members, expert
+slabs and ragged sizes.  The shapes come from
 a fixed seed, so every run checks the same sets."""
 from __future__ import annotations
 
@@ -33,11 +34,32 @@ def _random_set(seed):
     return shapes
 
 
+def _random_large_set(seed):
+    """m in [512, 1100] and n in [m, 3m]: single steps with the single-product
+    A^2 of the first steps when n < 2m, grouped steps when n >= 2m."""
+    rng = random.Random(seed)
+    shapes = []
+    for _ in range(rng.randint(1, 3)):
+        m = rng.randint(512, 1100)
+        n = rng.randint(m, 3 * m)
+        shapes.append((m, n) if rng.random() < 0.6 else (n, m))
+    return shapes
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_random_bf16_sets(seed):
     shapes = _random_set(seed)
     print(f"[random] seed {seed}: {shapes}", flush=True)
     wl = WL.custom(shapes, dtype=torch.bfloat16, g_std=1e-2, number=200 + seed)
+    run_and_compare(wl, steps=2)
+    ns_and_compare(wl)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_large_bf16_sets(seed):
+    shapes = _random_large_set(400 + seed)
+    print(f"[random] large seed {seed}: {shapes}", flush=True)
+    wl = WL.custom(shapes, dtype=torch.bfloat16, g_std=1e-3, number=400 + seed)
     run_and_compare(wl, steps=2)
     ns_and_compare(wl)
 

@@ -73,9 +73,9 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
 bool mfma_grouped(int64_t m, int64_t n) {
   // Only where grouped steps have been shown to keep O as accurate as single
   // steps (m >= 512, wide shapes), and where the saving outweighs the extra
-  // launches and the m x m epilogue traffic: pairs at n = 1.33 m
-  // (8 x [1536, 2048]) measured 15% slower than single steps, at n = 3.5 m
-  // ([8192, 28672], [4096, 14336]) 20-23% faster.
+  // launches and the m x m epilogue traffic: at n = 1.33 m (8 x [1536, 2048])
+  // grouped steps measured 20% slower than single steps (pairs 15%), at
+  // n = 3.5 m ([8192, 28672], [4096, 14336]) 35-40% faster.
   return m >= 512 && n >= 2 * m;
 }
 

@@ -15,6 +15,9 @@
 //                     in bf16 and the diagonal in fp32
 //   apply (MFMA)      X' = Poff Xt^T + diag(Pd) X; stores X' and X'^T in bf16,
 //                     or on the last step O (fp32) or the weight update
+// Wide bf16 groups (m >= 512, n >= 2 m) take several steps per Gram and
+// apply (ns_group_bf16): between them, m x m products form T = P A and
+// A' = P T (EpiSymMul) and R = P' R (EpiPairR), and the apply uses R.
 // The fp32 path runs the same sequence with fp32 FMA tiles and a full fp32 P.
 //
 // The NS step itself (A = X X^T; X <- aX + (bA + cA^2)X) is Newton-Schulz on

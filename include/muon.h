@@ -70,7 +70,8 @@ typedef enum {
   MUON_ERR_PLAN_MISMATCH = 4, /* n_params or shapes differ from the plan's */
   MUON_ERR_WORKSPACE = 5,     /* workspace null, too small or misaligned */
   MUON_ERR_HIP = 6,           /* a HIP runtime call or kernel launch failed */
-  MUON_ERR_ALIGNMENT = 7      /* a tensor pointer is not 16-byte aligned */
+  MUON_ERR_ALIGNMENT = 7,     /* a tensor pointer is not 16-byte aligned */
+  MUON_ERR_TIMEOUT = 8        /* an earlier skinny-path launch on this device timed out */
 } muon_status;
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
@@ -97,7 +98,8 @@ typedef struct muon_plan_s* muon_plan;
  *   out       : receives the plan.
  * Matrices are grouped by (min(rows,cols), max(rows,cols)); tall matrices
  * (rows > cols) join the group of their transpose and are handled in the wide
- * orientation.  The device is queried once, for its compute-unit count. */
+ * orientation.  No HIP call is made: the device is first queried (compute
+ * units, co-resident capacity) by the first muon_step / muon_ns on it. */
 muon_status muon_plan_create(const muon_shape* shapes, int32_t n_params, muon_dtype param_dt,
                              muon_dtype grad_dt, muon_dtype mom_dt, muon_plan* out);
 
@@ -124,7 +126,8 @@ muon_status muon_plan_group_info(muon_plan plan, int32_t g, int64_t* m, int64_t*
  *   shapes     : must equal the plan's shapes (checked).
  *   lr, wd, scale, mu : finite; mu in [0, 1); nesterov 0 or 1.
  *   a, b, c    : NS polynomial coefficients, finite.
- *   ns_steps   : 0 .. 16.
+ *   ns_steps   : 0 .. 16 (the accuracy stated above is measured for the
+ *                workloads' 5 steps; it is checked on the GPU up to 16).
  *   workspace  : device buffer of at least muon_plan_workspace_bytes(),
  *                256-byte aligned, zero-filled once before first use.
  * Tensor results do not depend on how matrices are grouped or batched:
@@ -216,10 +219,28 @@ muon_status muon_adamw_step(void* const* params, const void* const* grads, float
                             void* stream);
 
 /* ---- Diagnostics of the skinny path ---------------------------------------
- * Its cross-workgroup waits are bounded.  If one times out (the co-residency
- * the launch relies on was not granted, or the wait limit is too small), the
- * kernel raises a flag in the workspace, still runs to completion, and the
- * results of that call are invalid. */
+ * The skinny path (bf16, min(rows, cols) <= 32) runs one persistent launch
+ * per chunk whose workgroups exchange partial sums, so they must all be
+ * resident at once.  muon_step / muon_ns check, before enqueueing anything,
+ * that every chunk fits the device's co-resident capacity (compute units x
+ * workgroups per unit from the occupancy query) and return MUON_ERR_HIP
+ * otherwise.  The waits are bounded all the same: if one times out (another
+ * stream's kernels held compute units, or the wait limit is too small), that
+ * workgroup leaves its part of W (muon_step) or O (muon_ns) unwritten, the
+ * momenta of the call are already updated, the launch still runs to
+ * completion, and two flags are raised:
+ *   - a word in the workspace, read by muon_workspace_status;
+ *   - a host-visible word of the device (pinned host memory allocated by the
+ *     first muon_step / muon_ns call on the device that is not being
+ *     recorded into a graph).  The next muon_step / muon_ns call on the
+ *     device returns MUON_ERR_TIMEOUT, enqueues nothing and clears it;
+ *     muon_poll_timeout reads and clears it without a call. */
+
+/* Sets *timed_out to 1 if a skinny-path launch on the current device that
+ * has completed by now timed out since the word was last cleared, else 0,
+ * and clears it.  No synchronisation: synchronise the stream first to cover
+ * every launch enqueued so far. */
+muon_status muon_poll_timeout(int32_t* timed_out);
 
 /* Synchronises `stream` (the host waits for it), sets *timed_out to 1 if any
  * call on this workspace timed out since the last check, else 0, and clears

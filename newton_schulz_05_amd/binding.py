@@ -28,12 +28,13 @@ STATUS = {
     5: "MUON_ERR_WORKSPACE",
     6: "MUON_ERR_HIP",
     7: "MUON_ERR_ALIGNMENT",
+    8: "MUON_ERR_TIMEOUT",
 }
 
 EXPORTS = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes",
            "muon_plan_num_groups", "muon_plan_group_info", "muon_step", "muon_ns",
            "muon_plan_num_matrices", "muon_plan_assign", "muon_shard_update", "muon_adamw_step",
-           "muon_workspace_status", "muon_set_wait_limit",
+           "muon_workspace_status", "muon_set_wait_limit", "muon_poll_timeout",
            "muon_status_str", "muon_last_error_detail", "muon_version"]
 
 
@@ -94,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_workspace_status.restype = i32
     lib.muon_set_wait_limit.argtypes = [ctypes.c_uint32]
     lib.muon_set_wait_limit.restype = None
+    lib.muon_poll_timeout.argtypes = [P(i32)]
+    lib.muon_poll_timeout.restype = i32
     lib.muon_status_str.argtypes = [i32]
     lib.muon_status_str.restype = ctypes.c_char_p
     lib.muon_last_error_detail.argtypes = []
@@ -380,6 +383,15 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr: float, betas=(0.9, 0
     params/grads share a dtype (bf16 or fp32); the moment buffers are fp32."""
     AdamWGroup(params, grads, exp_avgs, exp_avg_sqs).step(lr=lr, betas=betas, eps=eps, wd=wd, step=step,
                                                           stream=stream)
+
+
+def poll_timeout() -> bool:
+    """True if a skinny-path launch on the current device that has completed
+    by now timed out since the last check (muon_poll_timeout); clears the
+    report.  No synchronisation: synchronise first to cover every launch."""
+    flag = ctypes.c_int32()
+    _check(load_library().muon_poll_timeout(ctypes.byref(flag)))
+    return bool(flag.value)
 
 
 def set_wait_limit(polls: int) -> None:

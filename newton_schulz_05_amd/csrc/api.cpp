@@ -1,6 +1,8 @@
 // C ABI entry points (include/muon.h): validation, per-chunk descriptor
-// tables, and the launch sequence on the caller's stream.  No device memory is
-// allocated or freed here and the host never waits for the device.
+// tables, and the launch sequence on the caller's stream.  The step entry
+// points allocate and free no device memory and never wait for the device;
+// the only allocation is one 4-byte pinned host word per device, made on the
+// first eager step (the skinny path's timeout report).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -13,6 +15,7 @@
 #include "../../include/muon.h"
 #include "launch.hpp"
 #include "plan.hpp"
+#include "validate.hpp"
 
 struct muon_plan_s {
   muon::Plan p;
@@ -48,78 +51,78 @@ bool capturing(hipStream_t st) {
   return hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
 }
 
-// Compute-unit count of the current device, per device id.
-std::mutex g_cu_mu;
-std::vector<int> g_cus;  // -1 = not queried
+// Per-device state: compute units, the skinny kernel's co-resident
+// capacity, and a host-visible word (pinned host memory) that a skinny
+// workgroup sets when one of its waits times out.
+struct DevState {
+  int cus = -1;
+  int skinny_cap = -1;
+  uint32_t* host_flag = nullptr;  // hipHostMalloc'd, 4 bytes; null until first eager step
+  bool flag_tried = false;
+};
+std::mutex g_dev_mu;
+std::vector<DevState> g_dev;
 
-muon_status device_cus(int* cus) {
+// Queries the current device once and returns its state.  `allow_alloc`: the
+// host-visible flag may be allocated (never while the stream is captured).
+muon_status device_state(bool allow_alloc, DevState* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
-  std::lock_guard<std::mutex> lk(g_cu_mu);
-  if (int(g_cus.size()) <= dev) g_cus.resize(dev + 1, -1);
-  if (g_cus[dev] < 0) {
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (int(g_dev.size()) <= dev) g_dev.resize(dev + 1);
+  DevState& d = g_dev[dev];
+  if (d.cus < 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       return fail(MUON_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
-    g_cus[dev] = n;
+    const int per_cu = muon::skinny_max_blocks_per_cu();
+    if (per_cu <= 0) return fail(MUON_ERR_HIP, "occupancy query of the skinny kernel failed");
+    d.cus = n;
+    d.skinny_cap = n * per_cu;
   }
-  *cus = g_cus[dev];
-  return MUON_OK;
-}
-
-// Co-resident workgroup capacity of the skinny kernel on the current device.
-muon_status skinny_capacity(int* cap) {
-  int cus = 0;
-  if (muon_status s = device_cus(&cus); s != MUON_OK) return s;
-  *cap = cus * muon::skinny_max_blocks_per_cu();
-  return MUON_OK;
-}
-
-bool finite(float x) { return std::isfinite(x); }
-
-muon_status check_shapes(const muon::Plan& P, const muon_shape* shapes, int32_t n_params) {
-  if (n_params != (int32_t)P.shapes.size())
-    return fail(MUON_ERR_PLAN_MISMATCH, "n_params " + std::to_string(n_params) + " != plan's " +
-                                            std::to_string(P.shapes.size()));
-  if (!shapes) return fail(MUON_ERR_INVALID_ARG, "shapes is null");
-  for (int32_t i = 0; i < n_params; ++i) {
-    const muon_shape& a = shapes[i];
-    const muon_shape& b = P.shapes[i];
-    if (a.batch != b.batch || a.rows != b.rows || a.cols != b.cols)
-      return fail(MUON_ERR_PLAN_MISMATCH, "shape of parameter " + std::to_string(i) + " differs from the plan");
+  if (allow_alloc && !d.flag_tried) {
+    d.flag_tried = true;
+    void* p = nullptr;
+    if (hipHostMalloc(&p, sizeof(uint32_t), hipHostMallocDefault) == hipSuccess && p) {
+      *(volatile uint32_t*)p = 0u;
+      d.host_flag = (uint32_t*)p;
+    }
   }
+  *out = d;
   return MUON_OK;
 }
 
-muon_status check_ptrs(const void* const* ptrs, int32_t n, const char* what) {
-  if (!ptrs) return fail(MUON_ERR_INVALID_ARG, std::string(what) + " array is null");
-  for (int32_t i = 0; i < n; ++i) {
-    if (!ptrs[i]) return fail(MUON_ERR_INVALID_ARG, std::string(what) + "[" + std::to_string(i) + "] is null");
-    if ((reinterpret_cast<uintptr_t>(ptrs[i]) & 15u) != 0)
-      return fail(MUON_ERR_ALIGNMENT, std::string(what) + "[" + std::to_string(i) + "] is not 16-byte aligned");
+// Reads and clears the host-visible timeout word of the current device.
+bool take_timeout(const DevState& d) {
+  if (!d.host_flag) return false;
+  return __atomic_exchange_n(d.host_flag, 0u, __ATOMIC_ACQ_REL) != 0u;
+}
+
+// Device checks done before anything is enqueued: every skinny chunk must
+// fit the device's co-resident capacity.
+muon_status check_device(const muon::Plan& P, const DevState& d) {
+  for (const muon::Group& grp : P.groups) {
+    if (grp.path != muon::PATH_SKINNY) continue;
+    const int64_t need = int64_t(grp.max_chunk) * grp.slabs;
+    if (need > d.skinny_cap)
+      return fail(MUON_ERR_HIP, "device holds only " + std::to_string(d.skinny_cap) +
+                                    " co-resident workgroups of the skinny kernel; a chunk needs " +
+                                    std::to_string(need));
   }
   return MUON_OK;
 }
 
 size_t elem_size(muon_dtype d) { return d == MUON_BF16 ? 2 : 4; }
 
-// Enqueue every chunk of every group.  `w`, `g`, `m` are per-parameter device
-// pointers (m may be null for muon_ns).
+// Enqueue every chunk of every group (arguments already validated).  `w`,
+// `g`, `m` are per-parameter device pointers (m may be null for muon_ns).
 muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, void* const* m,
-                    const muon::StepScalars& sc, void* workspace, hipStream_t st) {
+                    const muon::StepScalars& sc, void* workspace, hipStream_t st, const DevState& dev) {
   using namespace muon;
   uint8_t* ws = (uint8_t*)workspace;
   const size_t pes = elem_size(P.param_dt);
+  const bool cap = capturing(st);
   for (const Group& grp : P.groups) {
-    if (grp.path == PATH_SKINNY) {
-      int cap = 0;
-      muon_status s = skinny_capacity(&cap);
-      if (s != MUON_OK) return s;
-      if (int64_t(grp.max_chunk) * grp.slabs > cap)
-        return fail(MUON_ERR_HIP, "device holds only " + std::to_string(cap) +
-                                      " co-resident workgroups of the skinny kernel; a chunk needs " +
-                                      std::to_string(int64_t(grp.max_chunk) * grp.slabs));
-    }
     for (const Chunk& ch : grp.chunks) {
       MatTable tab;
       std::memset(&tab, 0, sizeof(tab));
@@ -147,7 +150,8 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         a.spin_limit = g_spin_limit.load();
         a.epoch = 0;
         a.epoch_dev = nullptr;
-        if (capturing(st)) {
+        a.host_flag = dev.host_flag;
+        if (cap) {
           uint32_t* counter = a.sync + muon::kSyncEpochWord;
           e = muon::run_epoch_bump(counter, st);
           a.epoch_dev = counter;
@@ -169,7 +173,7 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         a.tile = grp.tile;
         a.bf16 = (grp.path == PATH_MFMA);
         a.grouped = grp.grouped;
-        if (muon_status s = device_cus(&a.cus); s != MUON_OK) return s;
+        a.cus = dev.cus;
         e = run_large(a, st);
       }
       if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -178,20 +182,17 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
   return MUON_OK;
 }
 
-muon_status check_workspace(const muon::Plan& P, void* workspace, size_t bytes) {
-  if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is null");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(MUON_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  if (bytes < P.ws_bytes)
-    return fail(MUON_ERR_WORKSPACE, "workspace has " + std::to_string(bytes) + " bytes, needs " +
-                                        std::to_string(P.ws_bytes));
-  return MUON_OK;
-}
-
-muon_status check_coeffs(float a, float b, float c, int32_t ns_steps) {
-  if (!finite(a) || !finite(b) || !finite(c)) return fail(MUON_ERR_INVALID_ARG, "NS coefficients must be finite");
-  if (ns_steps < 0 || ns_steps > 16) return fail(MUON_ERR_INVALID_ARG, "ns_steps must be in 0..16");
-  return MUON_OK;
+// Device checks, the timeout report of earlier calls, then the launches.
+muon_status enqueue(const muon::Plan& P, void* const* w, const void* const* g, void* const* m,
+                    const muon::StepScalars& sc, void* workspace, hipStream_t st) {
+  DevState dev;
+  if (muon_status s = device_state(!capturing(st), &dev); s != MUON_OK) return s;
+  if (muon_status s = check_device(P, dev); s != MUON_OK) return s;
+  if (take_timeout(dev))
+    return fail(MUON_ERR_TIMEOUT, "an earlier skinny-path launch on this device timed out waiting for its "
+                                  "workgroups; its W (or O) was left partly unwritten and its momenta were "
+                                  "updated (nothing was enqueued by this call)");
+  return run_all(P, w, g, m, sc, workspace, st, dev);
 }
 
 }  // namespace
@@ -263,16 +264,11 @@ muon_status muon_plan_assign(muon_plan plan, int32_t n_ranks, int32_t* owner, in
 
 muon_status muon_shard_update(void* w_shard, muon_dtype dt, const float* o_full, int64_t offset, int64_t len,
                               float lr, float wd, float scale, void* stream) {
-  if (dt != MUON_F32 && dt != MUON_BF16) return fail(MUON_ERR_DTYPE, "dt must be MUON_F32 or MUON_BF16");
-  if (offset < 0 || len < 0) return fail(MUON_ERR_INVALID_ARG, "offset and len must be >= 0");
-  if (!finite(lr) || !finite(wd) || !finite(scale)) return fail(MUON_ERR_INVALID_ARG, "lr, wd and scale must be finite");
-  if (len == 0) return MUON_OK;
-  if (!w_shard || !o_full) return fail(MUON_ERR_INVALID_ARG, "null w_shard or o_full");
-  const size_t es = (dt == MUON_BF16) ? 2 : 4;
-  const char* w0 = (const char*)w_shard;
-  const char* o0 = (const char*)(o_full + offset);
-  if (w0 < o0 + size_t(len) * 4 && o0 < w0 + size_t(len) * es)
-    return fail(MUON_ERR_INVALID_ARG, "w_shard and o_full overlap");
+  std::string d;
+  bool nothing = false;
+  muon_status s = muon::validate_shard_update(w_shard, dt, o_full, offset, len, lr, wd, scale, &nothing, &d);
+  if (s != MUON_OK) return fail(s, d);
+  if (nothing) return MUON_OK;
   hipError_t e = muon::run_shard_update(w_shard, dt == MUON_BF16, o_full + offset, len, lr, wd, scale,
                                         (hipStream_t)stream);
   if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -282,24 +278,9 @@ muon_status muon_shard_update(void* w_shard, muon_dtype dt, const float* o_full,
 muon_status muon_adamw_step(void* const* params, const void* const* grads, float* const* exp_avg,
                             float* const* exp_avg_sq, const int64_t* numels, int32_t n, muon_dtype dt,
                             float lr, float b1, float b2, float eps, float wd, int64_t step, void* stream) {
-  if (dt != MUON_F32 && dt != MUON_BF16) return fail(MUON_ERR_DTYPE, "dt must be MUON_F32 or MUON_BF16");
-  if (n < 0) return fail(MUON_ERR_INVALID_ARG, "n must be >= 0");
-  if (n > 0 && (!params || !grads || !exp_avg || !exp_avg_sq || !numels))
-    return fail(MUON_ERR_INVALID_ARG, "null pointer array");
-  if (!finite(lr) || !finite(b1) || !finite(b2) || !finite(eps) || !finite(wd))
-    return fail(MUON_ERR_INVALID_ARG, "lr, b1, b2, eps and wd must be finite");
-  if (!(b1 >= 0.f && b1 < 1.f && b2 >= 0.f && b2 < 1.f)) return fail(MUON_ERR_INVALID_ARG, "b1 and b2 must be in [0, 1)");
-  if (!(eps > 0.f)) return fail(MUON_ERR_INVALID_ARG, "eps must be > 0");
-  if (step < 1) return fail(MUON_ERR_INVALID_ARG, "step must be >= 1");
-  for (int32_t i = 0; i < n; ++i) {
-    if (numels[i] < 0) return fail(MUON_ERR_SHAPE, "numels[" + std::to_string(i) + "] < 0");
-    if (numels[i] == 0) continue;
-    const void* ptrs[4] = {params[i], grads[i], exp_avg[i], exp_avg_sq[i]};
-    for (const void* q : ptrs)
-      if (!q) return fail(MUON_ERR_INVALID_ARG, "null tensor pointer at " + std::to_string(i));
-      else if ((uintptr_t)q % 4 != 0) return fail(MUON_ERR_ALIGNMENT, "tensor " + std::to_string(i) + " not 4-byte aligned");
-    if (numels[i] > (int64_t(1) << 40)) return fail(MUON_ERR_SHAPE, "tensor too large");
-  }
+  std::string d;
+  muon_status vs = muon::validate_adamw(params, grads, exp_avg, exp_avg_sq, numels, n, dt, lr, b1, b2, eps, wd, step, &d);
+  if (vs != MUON_OK) return fail(vs, d);
   // step size and bias corrections in double, rounded once to fp32
   const double t = double(step);
   muon::AdamScalars sc;
@@ -346,8 +327,9 @@ muon_status muon_workspace_status(muon_plan plan, void* workspace, size_t worksp
                                   int32_t* timed_out) {
   if (!plan || !timed_out) return fail(MUON_ERR_INVALID_ARG, "null plan or output pointer");
   const muon::Plan& P = plan->p;
-  muon_status s = check_workspace(P, workspace, workspace_bytes);
-  if (s != MUON_OK) return s;
+  std::string d;
+  muon_status s = muon::check_workspace(P, workspace, workspace_bytes, &d);
+  if (s != MUON_OK) return fail(s, d);
   const hipStream_t st = (hipStream_t)stream;
   uint32_t* flag = (uint32_t*)((uint8_t*)workspace + P.ws_sync_off) + muon::kSyncErrWord;
   uint32_t h = 0;
@@ -366,39 +348,38 @@ muon_status muon_workspace_status(muon_plan plan, void* workspace, size_t worksp
 
 void muon_set_wait_limit(uint32_t polls) { g_spin_limit.store(polls ? polls : kSpinLimit); }
 
+muon_status muon_poll_timeout(int32_t* timed_out) {
+  if (!timed_out) return fail(MUON_ERR_INVALID_ARG, "null output pointer");
+  *timed_out = 0;
+  DevState dev;
+  if (muon_status s = device_state(false, &dev); s != MUON_OK) return s;
+  *timed_out = take_timeout(dev) ? 1 : 0;
+  return MUON_OK;
+}
+
 muon_status muon_step(muon_plan plan, void* const* param_ptrs, const void* const* grad_ptrs,
                       void* const* mom_ptrs, const muon_shape* shapes, int32_t n_params, float lr,
                       float mu, int32_t nesterov, float wd, float a, float b, float c, int32_t ns_steps,
                       float scale, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!plan) return fail(MUON_ERR_INVALID_ARG, "null plan");
-  const muon::Plan& P = plan->p;
-  muon_status s = check_shapes(P, shapes, n_params);
-  if (s != MUON_OK) return s;
-  if ((s = check_ptrs((const void* const*)param_ptrs, n_params, "param_ptrs")) != MUON_OK) return s;
-  if ((s = check_ptrs(grad_ptrs, n_params, "grad_ptrs")) != MUON_OK) return s;
-  if ((s = check_ptrs((const void* const*)mom_ptrs, n_params, "mom_ptrs")) != MUON_OK) return s;
-  if (!finite(lr) || !finite(mu) || !finite(wd) || !finite(scale))
-    return fail(MUON_ERR_INVALID_ARG, "lr, mu, wd and scale must be finite");
-  if (nesterov != 0 && nesterov != 1) return fail(MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1");
-  if ((s = check_coeffs(a, b, c, ns_steps)) != MUON_OK) return s;
-  if ((s = check_workspace(P, workspace, workspace_bytes)) != MUON_OK) return s;
+  std::string d;
+  const muon::Plan* P = plan ? &plan->p : nullptr;
+  muon_status s = muon::validate_step(P, param_ptrs, grad_ptrs, mom_ptrs, shapes, n_params, lr, mu, nesterov, wd,
+                                      a, b, c, ns_steps, scale, workspace, workspace_bytes, &d);
+  if (s != MUON_OK) return fail(s, d);
   muon::StepScalars sc{lr, mu, wd, scale, a, b, c, nesterov, ns_steps, 0};
-  return run_all(P, param_ptrs, grad_ptrs, mom_ptrs, sc, workspace, (hipStream_t)stream);
+  return enqueue(*P, param_ptrs, grad_ptrs, mom_ptrs, sc, workspace, (hipStream_t)stream);
 }
 
 muon_status muon_ns(muon_plan plan, const void* const* in_ptrs, float* const* out_ptrs,
                     const muon_shape* shapes, int32_t n_params, float a, float b, float c,
                     int32_t ns_steps, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!plan) return fail(MUON_ERR_INVALID_ARG, "null plan");
-  const muon::Plan& P = plan->p;
-  muon_status s = check_shapes(P, shapes, n_params);
-  if (s != MUON_OK) return s;
-  if ((s = check_ptrs(in_ptrs, n_params, "in_ptrs")) != MUON_OK) return s;
-  if ((s = check_ptrs((const void* const*)out_ptrs, n_params, "out_ptrs")) != MUON_OK) return s;
-  if ((s = check_coeffs(a, b, c, ns_steps)) != MUON_OK) return s;
-  if ((s = check_workspace(P, workspace, workspace_bytes)) != MUON_OK) return s;
+  std::string d;
+  const muon::Plan* P = plan ? &plan->p : nullptr;
+  muon_status s = muon::validate_ns(P, in_ptrs, out_ptrs, shapes, n_params, a, b, c, ns_steps, workspace,
+                                    workspace_bytes, &d);
+  if (s != MUON_OK) return fail(s, d);
   muon::StepScalars sc{0.f, 0.f, 0.f, 1.f, a, b, c, 0, ns_steps, 1};
-  return run_all(P, (void* const*)out_ptrs, in_ptrs, nullptr, sc, workspace, (hipStream_t)stream);
+  return enqueue(*P, (void* const*)out_ptrs, in_ptrs, nullptr, sc, workspace, (hipStream_t)stream);
 }
 
 const char* muon_status_str(muon_status s) {
@@ -411,12 +392,13 @@ const char* muon_status_str(muon_status s) {
     case MUON_ERR_WORKSPACE: return "MUON_ERR_WORKSPACE";
     case MUON_ERR_HIP: return "MUON_ERR_HIP";
     case MUON_ERR_ALIGNMENT: return "MUON_ERR_ALIGNMENT";
+    case MUON_ERR_TIMEOUT: return "MUON_ERR_TIMEOUT";
   }
   return "MUON_ERR_UNKNOWN";
 }
 
 const char* muon_last_error_detail(void) { return g_detail.c_str(); }
 
-int32_t muon_version(void) { return 100; }
+int32_t muon_version(void) { return 200; }
 
 }  // extern "C"

@@ -87,8 +87,10 @@ __device__ __forceinline__ float block_sum_256(float v, float* lds4) {
 // A buffer resource bounds every access by its byte size: loads outside it
 // return 0 and stores outside it are dropped.  An element index of kOob
 // (times an element size of 2 or 4 bytes: 1 or 2 GiB) masks a lane without a
-// branch for any buffer smaller than 1 GiB.
+// branch for any buffer smaller than 1 GiB; kOobByte is the same mask as a
+// byte offset (2 GiB), for accesses indexed in bytes whatever their width.
 constexpr uint32_t kOob = 0x20000000u;
+constexpr uint32_t kOobByte = 0x80000000u;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);

@@ -34,7 +34,11 @@ namespace muon {
 // ============================================================================
 // One 64x64 tile of the matrix in its stored orientation [rows][cols] per
 // block; the grid covers the padded extent so that the padding of X and Xt is
-// written with zeros.
+// written with zeros.  The sum of squares of a tile that holds matrix
+// elements goes to slot (r0 / 64) * ceil(cols / 64) + c0 / 64: the slots, and
+// with them the order in which norm_kernel adds them, depend on the stored
+// shape alone and not on the padding (which follows the GEMM tile, and so
+// the group the matrix is in).  Tiles of padding only write no slot.
 template <typename PT, typename XT>
 __global__ __launch_bounds__(256) void momentum_kernel(MatTable tab, StepScalars sc, int tilesR,
                                                        int tilesC, XT* __restrict__ X,
@@ -51,6 +55,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(MatTable tab, StepScalars
   const int tile = blockIdx.x;
   const int tC = tr ? tilesR : tilesC;                       // tiles per stored row
   const int64_t r0 = int64_t(tile / tC) * 64, c0 = int64_t(tile % tC) * 64;
+  // norm slot of this tile, or -1 for a tile of padding only
+  const int64_t slot = (r0 < rows && c0 < cols) ? (r0 / 64) * ((cols + 63) / 64) + c0 / 64 : -1;
   const int t = threadIdx.x;
   const int cg = t & 15, rg = t >> 4;
   const PT* G = (const PT*)tab.e[z].g;
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(MatTable tab, StepScalars
         *(u32x4*)(trn + (c0 + lc) * ldt + r0 + 8 * cgrp) = tw;
       }
       const float tot = block_sum_256(ss, red);
-      if (t == 0) normpart[int64_t(z) * tiles + tile] = tot;
+      if (t == 0) normpart[int64_t(z) * tiles + slot] = tot;
       return;
     }
   }
@@ -151,10 +157,12 @@ __global__ __launch_bounds__(256) void momentum_kernel(MatTable tab, StepScalars
     }
   }
   const float tot = block_sum_256(ss, red);
-  if (t == 0) normpart[int64_t(z) * tiles + tile] = tot;
+  if (t == 0 && slot >= 0) normpart[int64_t(z) * tiles + slot] = tot;
 }
 
-// s = 1 / (sqrt(sum of squares) + eps); scal[z] = {s, s^2, sumsq, 0}
+// s = 1 / (sqrt(sum of squares) + eps); scal[z] = {s, s^2, sumsq, 0}.
+// `tiles` = ceil(m / 64) * ceil(n / 64) slots per matrix, added per thread in
+// index order and then across threads in a fixed tree.
 __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ normpart, int64_t tiles,
                                                    float* __restrict__ scal) {
   __shared__ float red[4];

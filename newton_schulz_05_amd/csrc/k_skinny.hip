@@ -89,6 +89,10 @@ __device__ __forceinline__ void tri_ij(int e, int m, int& i, int& j) {
   j = r + e;
 }
 
+// every partial buffer (at most kSkinnyCapacity slabs of two parities) lies
+// below the byte offset that masks a lane
+static_assert(uint64_t(kSkinnyCapacity) * 2 * kPartW * 8 < kOobByte, "partial buffer reaches the lane mask");
+
 struct SkShared {
   uint16_t stage[4][32 * kLdr];   // per-wave transpose staging, column-major [col][row]
   // per-wave Gram partials; gathered slab partials; the m x m matrices of the
@@ -98,6 +102,7 @@ struct SkShared {
   float mat[2][32][33];
   u16x8 pop[2][2][64];            // Q operand registers per lane: [k-step][hi, lo][lane]
   float ss[4];
+  int fail;                       // set when a wait of this workgroup timed out
 };
 
 // One 16 x 16 quadrant of A B for 32 x 32 fp32 matrices in LDS (stride 33):
@@ -169,13 +174,15 @@ template <typename PT, int MODE, int KS>
 __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalars sc, int m, int64_t n,
                                                         int S, int64_t slab_w, float* __restrict__ part,
                                                         uint32_t* __restrict__ sync, unsigned spin_limit,
-                                                        uint32_t epoch_host, const uint32_t* __restrict__ epoch_dev) {
+                                                        uint32_t epoch_host, const uint32_t* __restrict__ epoch_dev,
+                                                        uint32_t* __restrict__ host_flag) {
   static_assert(sizeof(PT) == 2, "skinny path is bf16");
   // launches recorded into a graph read their number from the counter that
   // the one-thread kernel before them advanced; others get it from the host
   const uint32_t epoch = epoch_dev ? (kDeviceEpochBit | (*epoch_dev & (kDeviceEpochBit - 1))) : epoch_host;
   constexpr bool step_mode = MODE == 0;
   __shared__ SkShared sh;
+  if (threadIdx.x == 0) sh.fail = 0;  // read only after several barriers
   const int z = blockIdx.x / S, s = blockIdx.x % S;
   // copy this matrix's descriptor out of the argument block
   const bool tr = tab.tr[z] != 0;
@@ -374,7 +381,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       auto woff = [&](int j) -> uint32_t {
         const int idx = t + 256 * j;
         const int q = idx / nw, e = idx - q * nw;
-        return (idx < tot) ? (src + (q0 + q) * kPartW + (e < ntri ? e : 528)) * 8 : kOob * 8;
+        return (idx < tot) ? (src + (q0 + q) * kPartW + (e < ntri ? e : 528)) * 8 : kOobByte;
       };
       u32x2 w[kGather];
 #pragma unroll
@@ -386,7 +393,11 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
         for (int j = 0; j < kGather; ++j) ready &= (t + 256 * j >= tot) || (w[j][1] == tag);
         if (ready) break;
         if (++it > spin_limit) {
+          // give up: flag the workspace (and the host-visible word, if any),
+          // and leave W (or O) of this slab unwritten
+          sh.fail = 1;
           __hip_atomic_store(sync + kSyncErrWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (host_flag) __hip_atomic_store(host_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
           break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -492,7 +503,8 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
 
   // O for one block (16 values per lane) -> fp32 store or weight update
   const float keep = 1.0f - sc.lr * sc.wd, stepc = -sc.lr * sc.scale;
-  auto emit_block = [&](const f32x16& o, int q, const u32x4* wq) {
+  auto emit_block = [&](const f32x16& o, int q, bool failed) {
+    if (failed) return;  // a wait timed out: W (or O) keeps its contents
     const int lane = opaque(int(threadIdx.x)) & 63, h = lane >> 5, cl = lane & 31;
     if (full(q)) {
       // O through LDS (fp32, column-major, stride 33) to row-major vectors
@@ -551,10 +563,11 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   __builtin_amdgcn_s_setprio(0);
   {
     const int lane = opaque(int(threadIdx.x)) & 63;
+    const bool failed = sh.fail != 0;
 #pragma unroll
     for (int q = 0; q < kNB; ++q) {
       const f32x16 acc = apply(xw[q], lane);
-      emit_block(acc, q, nullptr);
+      emit_block(acc, q, failed);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -564,7 +577,7 @@ template <int MODE, int KS>
 static void launch_skinny(const SkinnyArgs& g, hipStream_t st) {
   const unsigned grid = unsigned(g.count * g.slabs);
   hipLaunchKernelGGL((skinny_kernel<uint16_t, MODE, KS>), dim3(grid), dim3(256), 0, st, g.tab, g.sc, g.m, g.n,
-                     g.slabs, g.slab_w, g.part, g.sync, g.spin_limit, g.epoch, g.epoch_dev);
+                     g.slabs, g.slab_w, g.part, g.sync, g.spin_limit, g.epoch, g.epoch_dev, g.host_flag);
 }
 
 hipError_t run_skinny(const SkinnyArgs& g, hipStream_t st) {

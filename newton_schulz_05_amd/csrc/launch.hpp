@@ -44,6 +44,7 @@ struct SkinnyArgs {
   unsigned spin_limit;
   uint32_t epoch;    // distinct per launch: tags the published partials
   const uint32_t* epoch_dev;  // if set, the epoch is read from here (graph capture)
+  uint32_t* host_flag;        // host-visible word set on a timed-out wait, or null
 };
 
 hipError_t run_large(const LargeArgs& a, hipStream_t st);

@@ -37,8 +37,9 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
   const int64_t mp = g.mp, np = g.np;
   L.x_stride = mp * np;
   L.a_stride = mp * mp;
-  // the momentum kernel's 64x64 tiles cover the padded matrix
-  L.tiles = (mp / kMomTile) * (np / kMomTile);
+  // norm slots: one per 64x64 momentum tile that holds matrix elements, so
+  // their number and order depend on (m, n) alone, not on the padding
+  L.tiles = ceil_div(g.m, kMomTile) * ceil_div(g.n, kMomTile);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   const size_t xb = size_t(count) * size_t(mp) * size_t(np) * es;

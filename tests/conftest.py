@@ -25,3 +25,21 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _no_skinny_timeout(request):
+    """After every GPU test: no skinny-path wait timed out during it (such a
+    launch leaves part of its output unwritten, so a test could otherwise
+    pass on stale values)."""
+    yield
+    if "gpu" not in request.keywords:
+        return
+    import torch
+    if not torch.cuda.is_available():
+        return
+    from newton_schulz_05_amd import binding as B
+    if B._lib is None:
+        return
+    torch.cuda.synchronize()
+    assert not B.poll_timeout(), "a skinny-path wait timed out during this test"

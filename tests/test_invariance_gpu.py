@@ -187,3 +187,36 @@ def test_partial_round_at_smaller_tile_is_bitwise_neutral(shapes):
         p1, m1 = _step([shapes[i]], [params[i].clone()], [[grads[0][i]], [grads[1][i]]], torch.bfloat16)
         assert torch.equal(p1[0], pg[i]), f"W[{i}] differs between the split and single-matrix grids"
         assert torch.equal(m1[0], mg[i])
+
+
+def test_padding_of_the_group_is_bitwise_neutral():
+    """Nine [2000, 2900] matrices (the last stored tall) take 256-tiles and
+    are padded to [2048, 3072]; one alone takes 128-tiles and [2048, 2944].
+    The momentum kernel's sum-of-squares slots and their summation order
+    follow the matrix's own 64 x 64 tiles, not the padded grid, so every bit
+    of W and M must agree."""
+    shapes = [(2000, 2900)] * 8 + [(2900, 2000)]
+    params, grads = _draw(shapes, torch.bfloat16, 79)
+    pg, mg = _step(shapes, [p.clone() for p in params], grads, torch.bfloat16)
+    for i in (0, 4, 8):
+        p1, m1 = _step([shapes[i]], [params[i].clone()], [[grads[0][i]], [grads[1][i]]], torch.bfloat16)
+        assert torch.equal(p1[0], pg[i]), f"W[{i}] differs between the grouped (256-tile) and alone (128-tile) runs"
+        assert torch.equal(m1[0], mg[i])
+
+
+@pytest.mark.parametrize("shapes,picks,chunks", [
+    ([(24, 1024)] * 170, (0, 56, 57, 113, 114, 169), 3),
+    ([(64, 200)] * 90, (0, 44, 45, 89), 2),
+], ids=["skinny_3_chunks", "mfma_2_chunks"])
+def test_chunking_is_bitwise_neutral(shapes, picks, chunks):
+    """A group larger than one launch's descriptor table is split into
+    chunks; every matrix must come out as it does stepped alone, whichever
+    chunk (first, last, either side of a boundary) holds it."""
+    plan = MuonPlan(shapes, torch.bfloat16)
+    assert plan.groups()[0]["n_chunks"] == chunks
+    params, grads = _draw(shapes, torch.bfloat16, 80)
+    pg, mg = _step(shapes, [p.clone() for p in params], grads, torch.bfloat16)
+    for i in picks:
+        p1, m1 = _step([shapes[i]], [params[i].clone()], [[grads[0][i]], [grads[1][i]]], torch.bfloat16)
+        assert torch.equal(p1[0], pg[i]), f"W[{i}] differs between the chunked group and alone"
+        assert torch.equal(m1[0], mg[i])

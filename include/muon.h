@@ -143,6 +143,29 @@ muon_status muon_step(muon_plan plan, void* const* param_ptrs, const void* const
                       float c, int32_t ns_steps, float scale, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* muon_step without a workspace argument, for callers that cannot allocate
+ * device memory (code recorded into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a file-scope device
+ * array of the library, 64 MiB per device, held until the process ends:
+ *   - plans whose muon_plan_workspace_bytes() exceeds 64 MiB are rejected
+ *     with MUON_ERR_WORKSPACE before anything is enqueued (the skinny path's
+ *     sets fit: 74 x [24, 10240] needs 6.5 MB; large MFMA groups do not);
+ *   - the first call on a device looks up the array's device address, clears
+ *     the array on `stream` and waits for it; that first call must not be
+ *     recorded into a graph (MUON_ERR_INVALID_ARG);
+ *   - every call on a device shares that device's array: calls that overlap
+ *     in time on one device (other streams, other host threads) race and give
+ *     undefined results; order them on one stream;
+ *   - no hipMalloc, hipFree or other allocating routine is called, and the
+ *     host-visible timeout word is used only if a muon_step / muon_ns call
+ *     already created it.
+ * Arguments, results and errors are otherwise those of muon_step; the
+ * results are bit-identical to muon_step's. */
+muon_status muon_step_noalloc(muon_plan plan, void* const* param_ptrs, const void* const* grad_ptrs,
+                              void* const* mom_ptrs, const muon_shape* shapes, int32_t n_params,
+                              float lr, float mu, int32_t nesterov, float wd, float a, float b,
+                              float c, int32_t ns_steps, float scale, void* stream);
+
 /* NS alone: out = NS(in) for every parameter, in fp32, same shapes as in.
  *   in_ptrs  : dtype param_dt (the NS input, e.g. a momentum), read only.
  *   out_ptrs : fp32 outputs.

@@ -34,7 +34,7 @@ STATUS = {
 EXPORTS = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes",
            "muon_plan_num_groups", "muon_plan_group_info", "muon_step", "muon_ns",
            "muon_plan_num_matrices", "muon_plan_assign", "muon_shard_update", "muon_adamw_step",
-           "muon_workspace_status", "muon_set_wait_limit", "muon_poll_timeout",
+           "muon_workspace_status", "muon_set_wait_limit", "muon_poll_timeout", "muon_step_noalloc",
            "muon_status_str", "muon_last_error_detail", "muon_version"]
 
 
@@ -81,6 +81,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_step.argtypes = [vp, P(vp), P(vp), P(vp), P(MuonShape), i32, f32, f32, i32, f32,
                               f32, f32, f32, i32, f32, vp, sz, vp]
     lib.muon_step.restype = i32
+    lib.muon_step_noalloc.argtypes = [vp, P(vp), P(vp), P(vp), P(MuonShape), i32, f32, f32, i32, f32,
+                                      f32, f32, f32, i32, f32, vp]
+    lib.muon_step_noalloc.restype = i32
     lib.muon_ns.argtypes = [vp, P(vp), P(vp), P(MuonShape), i32, f32, f32, f32, i32, vp, sz, vp]
     lib.muon_ns.restype = i32
     lib.muon_plan_num_matrices.argtypes = [vp, P(i64)]
@@ -263,6 +266,21 @@ class MuonPlan:
                              len(self.shapes), float(lr), float(mu), int(bool(nesterov)), float(wd),
                              a, b, c, int(ns_steps), float(scale), ctypes.c_void_p(workspace.data_ptr()),
                              workspace.numel(), ctypes.c_void_p(self._stream(stream))))
+
+    def step_noalloc(self, params, grads, moms, *, lr: float, mu: float = 0.95, nesterov: bool = True,
+                     wd: float = 0.0, coeffs=(3.4445, -4.7750, 2.0315), ns_steps: int = 5,
+                     scale: float = 1.0, stream=None) -> None:
+        """One Muon step without a workspace (muon_step_noalloc): the library's
+        64 MiB static device array serves as workspace, shared by every such
+        call on the device.  For plans whose workspace fits in it."""
+        lib = load_library()
+        self._check_tensors(params, self.dtype, "params")
+        self._check_tensors(grads, self.dtype, "grads")
+        self._check_tensors(moms, torch.float32, "moms")
+        a, b, c = (float(x) for x in coeffs)
+        _check(lib.muon_step_noalloc(self._h, _ptrs(params), _ptrs(grads), _ptrs(moms), self._cshapes,
+                                     len(self.shapes), float(lr), float(mu), int(bool(nesterov)), float(wd),
+                                     a, b, c, int(ns_steps), float(scale), ctypes.c_void_p(self._stream(stream))))
 
     def ns(self, inputs, outputs, *, coeffs=(3.4445, -4.7750, 2.0315), ns_steps: int = 5,
            workspace: Optional[torch.Tensor] = None, stream=None) -> None:

@@ -59,17 +59,19 @@ struct DevState {
   int skinny_cap = -1;
   uint32_t* host_flag = nullptr;  // hipHostMalloc'd, 4 bytes; null until first eager step
   bool flag_tried = false;
+  void* scratch = nullptr;        // device address of this device's copy of `scratch`
 };
+constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
-std::vector<DevState> g_dev;
+DevState g_dev[kMaxDevices];  // fixed storage: looking a device up allocates nothing
 
 // Queries the current device once and returns its state.  `allow_alloc`: the
 // host-visible flag may be allocated (never while the stream is captured).
 muon_status device_state(bool allow_alloc, DevState* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MUON_ERR_HIP, "device index beyond the library's table");
   std::lock_guard<std::mutex> lk(g_dev_mu);
-  if (int(g_dev.size()) <= dev) g_dev.resize(dev + 1);
   DevState& d = g_dev[dev];
   if (d.cus < 0) {
     int n = 0;
@@ -183,16 +185,56 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
 }
 
 // Device checks, the timeout report of earlier calls, then the launches.
+// `allow_alloc`: the host-visible timeout word may be allocated (first call).
 muon_status enqueue(const muon::Plan& P, void* const* w, const void* const* g, void* const* m,
-                    const muon::StepScalars& sc, void* workspace, hipStream_t st) {
+                    const muon::StepScalars& sc, void* workspace, hipStream_t st, bool allow_alloc = true) {
   DevState dev;
-  if (muon_status s = device_state(!capturing(st), &dev); s != MUON_OK) return s;
+  if (muon_status s = device_state(allow_alloc && !capturing(st), &dev); s != MUON_OK) return s;
   if (muon_status s = check_device(P, dev); s != MUON_OK) return s;
   if (take_timeout(dev))
     return fail(MUON_ERR_TIMEOUT, "an earlier skinny-path launch on this device timed out waiting for its "
                                   "workgroups; its W (or O) was left partly unwritten and its momenta were "
                                   "updated (nothing was enqueued by this call)");
   return run_all(P, w, g, m, sc, workspace, st, dev);
+}
+
+// ---- The allocation-free step (muon_step_noalloc) --------------------------
+// Its workspace is this file-scope device array, one copy per device, held
+// until the process ends.  In host code `scratch` only names the symbol: its
+// device address is taken once per device with hipGetSymbolAddress and kept
+// in DevState::scratch, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void zero_fill_kernel(uint4* p, size_t n16) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += size_t(gridDim.x) * blockDim.x)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+// Device address of the current device's scratch array, set up on the first
+// call on that device: the address is looked up, the array is cleared by a
+// fill kernel on `st` and the host waits for it (first call only, so it must
+// not be recorded into a graph).
+muon_status scratch_address(hipStream_t st, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MUON_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MUON_ERR_HIP, "device index beyond the library's table");
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevState& d = g_dev[dev];
+  if (!d.scratch) {
+    if (capturing(st))
+      return fail(MUON_ERR_INVALID_ARG, "the first muon_step_noalloc call on a device sets up its scratch "
+                                        "array and must not be recorded into a graph");
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+      return fail(MUON_ERR_HIP, "hipGetSymbolAddress(scratch) failed");
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, st, (uint4*)p, kScratchBytes / 16);
+    if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess)
+      return fail(MUON_ERR_HIP, "clearing the scratch array failed");
+    d.scratch = p;
+  }
+  *out = d.scratch;
+  return MUON_OK;
 }
 
 }  // namespace
@@ -368,6 +410,27 @@ muon_status muon_step(muon_plan plan, void* const* param_ptrs, const void* const
   if (s != MUON_OK) return fail(s, d);
   muon::StepScalars sc{lr, mu, wd, scale, a, b, c, nesterov, ns_steps, 0};
   return enqueue(*P, param_ptrs, grad_ptrs, mom_ptrs, sc, workspace, (hipStream_t)stream);
+}
+
+muon_status muon_step_noalloc(muon_plan plan, void* const* param_ptrs, const void* const* grad_ptrs,
+                              void* const* mom_ptrs, const muon_shape* shapes, int32_t n_params, float lr,
+                              float mu, int32_t nesterov, float wd, float a, float b, float c,
+                              int32_t ns_steps, float scale, void* stream) {
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "null plan");
+  if (plan->p.ws_bytes > kScratchBytes)
+    return fail(MUON_ERR_WORKSPACE, "the plan needs " + std::to_string(plan->p.ws_bytes) +
+                                        " bytes of workspace; the static scratch array holds " +
+                                        std::to_string(kScratchBytes) + " (use muon_step with a workspace)");
+  std::string d;
+  // every argument but the workspace, checked before any device work
+  muon_status s = muon::validate_step(&plan->p, param_ptrs, grad_ptrs, mom_ptrs, shapes, n_params, lr, mu, nesterov,
+                                      wd, a, b, c, ns_steps, scale, (const void*)uintptr_t(256), kScratchBytes, &d);
+  if (s != MUON_OK) return fail(s, d);
+  const hipStream_t st = (hipStream_t)stream;
+  void* ws = nullptr;
+  if ((s = scratch_address(st, &ws)) != MUON_OK) return s;
+  muon::StepScalars sc{lr, mu, wd, scale, a, b, c, nesterov, ns_steps, 0};
+  return enqueue(plan->p, param_ptrs, grad_ptrs, mom_ptrs, sc, ws, st, false);
 }
 
 muon_status muon_ns(muon_plan plan, const void* const* in_ptrs, float* const* out_ptrs,

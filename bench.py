@@ -227,14 +227,18 @@ def alg_flops(wl) -> float:
 
 
 def executed_flops(wl) -> float:
-    """MFMA flops the bf16 path executes for one step (symmetric outputs on
-    their upper tiles only; true m and n, padding not counted).  Mirrors the
-    library's schedule: A^2 as one product in NS steps k < min(3, steps - 2)
-    when m >= 512, as three split products otherwise; for m >= 512 and
-    n >= 2 m, steps taken in groups (the first min(4, steps - 1), then pairs,
-    then a single step), each with one Gram m^2 n, per step the m x m products
-    A^2 and, after the group's first step, T = P A, A' = P T and R = P R, and
-    one apply 2 m^2 n."""
+    """MFMA flops the bf16 path executes for one muon_step (symmetric outputs
+    on their upper tiles only; true m and n, padding not counted).  Mirrors
+    the library's schedule: all NS steps in one group when m < 512, else the
+    first min(4, N - 1), then pairs, then a single step; per group one Gram
+    m^2 n, per step A^2 (one product m^3 in steps k < min(3, N - 2) when
+    m >= 512, else three), after the group's first step the products
+    T = P A, A' = P T and R = P R (m^3 each), and one apply 2 m^2 n.  The
+    lo planes add products: the first Gram takes three (precise recipe,
+    m < 4096 or more than 5 steps), the chain products three each (precise),
+    and an apply one more
+    per lo plane it uses (X_0's in the first group, R's in the precise
+    recipe)."""
     N = wl.ns_steps
     tot = 0.0
     for s in wl.shapes:
@@ -244,17 +248,20 @@ def executed_flops(wl) -> float:
         if m <= 32:
             tot += b * (3.0 * m * m * n + m ** 3) * N
             continue
+        whole, precise = m < 512, (m < 4096 or N > 5)
         a2 = lambda k: (1 if (m >= 512 and k < min(3, N - 2)) else 3) * m ** 3  # noqa: E731
-        grouped = m >= 512 and n >= 2 * m
+        chain = 3 if precise else 1
         f, k = 0.0, 0
         while k < N:
-            if not grouped:
-                G = 1
+            if whole:
+                G = N - k
             elif k == 0:
                 G = N if N <= 2 else min(4, N - 1)
             else:
                 G = 2 if N - k >= 2 else 1
-            f += 3 * m * m * n + sum(a2(k + j) for j in range(G)) + 3 * (G - 1) * m ** 3
+            gram = (3 if (k == 0 and precise) else 1) * m * m * n
+            apply = (1 + (1 if k == 0 else 0) + (1 if precise else 0)) * 2 * m * m * n
+            f += gram + sum(a2(k + j) for j in range(G)) + 3 * chain * (G - 1) * m ** 3 + apply
             k += G
         tot += b * f
     return tot
@@ -304,14 +311,134 @@ def cpu_baseline(wl, budget_s: float):
             "sample": f"{n_params} parameter-steps of {wl.name} (fp64 NumPy, {el:.1f} s)"}
 
 
+def _skinny_only(plan, wl):
+    import torch
+    return all(g["m"] <= 32 for g in plan.groups()) and wl.dtype == torch.bfloat16
+
+
+def bench_step(wl, steps, warmup, dev="cuda", per_group=True, n_sets=None):
+    """Time `steps` muon_step calls over the whole parameter set of `wl`
+    (inputs resident in HBM, gradient sets drawn beforehand and cycled),
+    then the same number again with the apply launches timed by HIP events
+    on the launch stream.  Returns the measurements as a dict."""
+    import torch
+
+    from newton_schulz_05_amd import MuonPlan
+    from newton_schulz_05_amd import binding as B
+    from newton_schulz_05_amd import workloads as WL
+
+    big = wl.n_elements() > 500_000_000
+    plan = MuonPlan(wl.shapes, wl.dtype)
+    ws = plan.new_workspace(dev)
+    params = WL.make_params(wl, dev, dev)
+    moms = WL.make_moms(wl, dev)
+    n_sets = n_sets or (2 if big else 4)
+    gsets = [WL.make_grads(wl, s, dev, dev) for s in range(n_sets)]
+    torch.cuda.synchronize()
+    hyper = wl.hyper()
+    stream = torch.cuda.current_stream()
+    # tensors are validated once; each timed step is one C call
+    bound = [plan.bind(params, g, moms, workspace=ws) for g in gsets]
+    for s in range(warmup):
+        bound[s % n_sets].step(**hyper, stream=stream)
+    torch.cuda.synchronize()
+    # HIP events on the stream the kernels are launched on, around the K
+    # back-to-back steps (a per-step event would add a marker between kernels)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for s in range(steps):
+        bound[s % n_sets].step(**hyper, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    # a skinny-path wait that timed out would have left W partly unwritten
+    timed_out = plan.workspace_timed_out(ws, stream) or B.poll_timeout()
+    out = {"ms": ms, "wall_s": wall, "timed_out": timed_out, "plan": plan.groups()}
+    if not _skinny_only(plan, wl) and wl.dtype == torch.bfloat16:
+        # the same steps again with every apply bracketed by events
+        B.kernel_timing(True)
+        B.kernel_timing_read()
+        for s in range(steps):
+            bound[s % n_sets].step(**hyper, stream=stream)
+        torch.cuda.synchronize()
+        kt = B.kernel_timing_read()
+        B.kernel_timing(False)
+        out["apply"] = kt
+        timed_out = timed_out or plan.workspace_timed_out(ws, stream) or B.poll_timeout()
+        out["timed_out"] = timed_out
+    del bound, gsets, params, moms, ws
+    torch.cuda.empty_cache()
+    if per_group and len(out["plan"]) > 1:
+        out["groups"] = time_groups(wl, steps, warmup, dev)
+    return out
+
+
+def _roofline(wl, res):
+    """The dominant kernel against its bound.  Skinny sets: the single
+    persistent kernel per chunk (the whole step), HBM-bound, on the 14 B per
+    element compulsory bytes.  MFMA sets: the apply launches, bf16 MFMA on
+    their algorithmic flops (2 m^2 n per matrix per apply) over their
+    event-timed duration; executed flops (lo-plane products) beside them."""
+    import torch
+    ms = res["ms"]
+    if all(g["m"] <= 32 for g in res["plan"]) and wl.dtype == torch.bfloat16:
+        gbs = alg_bytes(wl) / (ms * 1e-3) / 1e9
+        tr = skinny_traffic_bytes() if wl.key == "c2" else None
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None if tr is None else round(tr),
+                "kernel": "skinny_kernel", "launches_per_step": sum(g["n_chunks"] for g in res["plan"])}
+    if wl.dtype != torch.bfloat16:
+        tf = alg_flops(wl) / (ms * 1e-3) / 1e12
+        return {"bound": "alu", "achieved": round(tf, 3), "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / F32_VALU_PEAK_TFLOPS, 6), "traffic": None, "kernel": "whole step"}
+    # the apply's MFMA work: one m x m by m x n product per pair of operand
+    # planes it multiplies (X_0's lo plane in the first group, R's in the
+    # precise recipe), true m and n (padding not counted), over the
+    # event-timed duration of the applies
+    kt = res["apply"]
+    ex = kt["exec_flops"] / (kt["ms"] * 1e-3) / 1e12
+    plain = kt["alg_flops"] / (kt["ms"] * 1e-3) / 1e12
+    steps = max(1, res.get("steps", 1))
+    n = max(1, kt["launches"])
+    return {"bound": "mfma", "achieved": round(ex, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ex / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "kernel": "gemm_bf16_kernel<*, *, EpiApplyBf16> (apply X' = R X)",
+            "launches_per_step": round(kt["launches"] / steps, 2),
+            "avg_launch_ms": round(kt["ms"] / n, 4),
+            "tflop_per_launch": round(kt["exec_flops"] / n / 1e12, 4),
+            "single_product_tflop_per_launch": round(kt["alg_flops"] / n / 1e12, 4),
+            "single_product_tflops": round(plain, 1),
+            "share_of_step": round(kt["ms"] / steps / res["ms"], 3)}
+
+
+def _summary(wl, res):
+    """ms, throughput and fraction of the bound of a whole step."""
+    import torch
+    ms = res["ms"]
+    tf = alg_flops(wl) / (ms * 1e-3) / 1e12
+    d = {"workload": wl.name, "ms_per_step": round(ms, 5), "alg_tflops": round(tf, 3)}
+    if all(g["m"] <= 32 for g in res["plan"]) and wl.dtype == torch.bfloat16:
+        gbs = alg_bytes(wl) / (ms * 1e-3) / 1e9
+        d.update(bound="hbm", gbs_compulsory=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        ex = executed_flops(wl) / (ms * 1e-3) / 1e12
+        d.update(bound="mfma", frac=round(tf / BF16_PEAK_TFLOPS, 4), executed_tflops=round(ex, 1),
+                 executed_frac=round(ex / BF16_PEAK_TFLOPS, 4))
+    return d
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads' whole-step figures reported beside the headline")
     ap.add_argument("--op", default="step", choices=["step", "ns", "shard_update", "adamw"],
                     help="step: the Muon step (default); ns: muon_ns alone on the workload; "
                          "shard_update / adamw: the companion kernels")
@@ -343,72 +470,21 @@ def main() -> int:
 
     import torch
 
-    from newton_schulz_05_amd import MuonPlan
     from newton_schulz_05_amd import workloads as WL
 
     wl = WL.WORKLOADS[args.config]
     big = args.config in ("c4", "c5")
     steps = args.steps if args.steps is not None else (10 if big else 100)
     warmup = args.warmup if args.warmup is not None else (2 if big else 10)
-    dev = "cuda"
-    plan = MuonPlan(wl.shapes, wl.dtype)
-    ws = plan.new_workspace(dev)
-    params = WL.make_params(wl, dev, dev)
-    moms = WL.make_moms(wl, dev)
-    n_sets = 2 if big else 4
-    gsets = [WL.make_grads(wl, s, dev, dev) for s in range(n_sets)]
-    torch.cuda.synchronize()
-    hyper = wl.hyper()
-    stream = torch.cuda.current_stream()
-
-    # tensors are validated once; each timed step is one C call
-    bound = [plan.bind(params, g, moms, workspace=ws) for g in gsets]
-    for s in range(warmup):
-        bound[s % n_sets].step(**hyper, stream=stream)
-    torch.cuda.synchronize()
-
-    # HIP events on the stream the kernels are launched on, around the K
-    # back-to-back steps (a per-step event would add a marker between kernels)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for s in range(steps):
-        bound[s % n_sets].step(**hyper, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / steps
+    res = bench_step(wl, steps, warmup)
+    res["steps"] = steps
+    if res["timed_out"]:
+        print("a skinny-path wait timed out during the timed steps: the results are invalid", file=sys.stderr)
+        return 3
+    ms = res["ms"]
     flops = alg_flops(wl)
     byt = alg_bytes(wl)
     tflops = flops / (ms * 1e-3) / 1e12
-
-    groups = plan.groups()
-    skinny_only = all(g["m"] <= 32 for g in groups) and wl.dtype == torch.bfloat16
-    if skinny_only:
-        # one persistent kernel per chunk; with one chunk the step is one launch
-        gbs = byt / (ms * 1e-3) / 1e9
-        tr = skinny_traffic_bytes() if args.config == "c2" else None
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None if tr is None else round(tr),
-                "kernel": "skinny_kernel", "launches_per_step": sum(g["n_chunks"] for g in groups)}
-    elif wl.dtype == torch.bfloat16:
-        # `achieved` counts the algorithmic work of the plain iteration; the
-        # MFMA work the kernels execute (split A^2 adds to it, paired steps
-        # take from it) is reported beside it
-        ex = executed_flops(wl) / (ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "whole step",
-                "executed_tflops": round(ex, 1), "executed_frac": round(ex / BF16_PEAK_TFLOPS, 4),
-                "executed_tflop_per_step": round(executed_flops(wl) / 1e12, 3)}
-    else:
-        roof = {"bound": "alu", "achieved": round(tflops, 3), "peak": F32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / F32_VALU_PEAK_TFLOPS, 6), "traffic": None, "kernel": "whole step"}
-
-    per_group = None
-    if len(groups) > 1:
-        per_group = time_groups(wl, steps, warmup, dev)
-
     out = {
         "metric": "Muon step ms & TFLOP/s (% bf16 MFMA peak / % HBM BW) for batched NS on [B,M,N]",
         "value": round(tflops, 3),
@@ -417,8 +493,8 @@ def main() -> int:
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms, 5),
-        "ms_per_step_wall": round(wall * 1e3 / steps, 5),
-        "wall_s": round(wall, 3),
+        "ms_per_step_wall": round(res["wall_s"] * 1e3 / steps, 5),
+        "wall_s": round(res["wall_s"], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -426,16 +502,41 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "matrices": wl.n_matrices(), "elements": wl.n_elements(),
                    "ns_steps": wl.ns_steps, "alg_tflop_per_step": flops / 1e12,
-                   "compulsory_gb_per_step": byt / 1e9, "hbm_gbs_compulsory": round(byt / (ms * 1e-3) / 1e9, 1),
-                   "parallelism": "single_gpu"},
-        "roofline": roof,
+                   "executed_tflop_per_step": round(executed_flops(wl) / 1e12, 3),
+                   "compulsory_gb_per_step": byt / 1e9, "parallelism": "single_gpu"},
+        "roofline": _roofline(wl, res),
+        "step": _summary(wl, res),
     }
-    if per_group is not None:
-        out["groups"] = per_group
+    if res.get("groups"):
+        out["groups"] = res["groups"]
+    if not args.no_extra:
+        # the other large and the skinny workload, whole-step figures only
+        extra = {}
+        for key in ("c5", "c2"):
+            if key == args.config:
+                continue
+            w2 = WL.WORKLOADS[key]
+            b2 = key in ("c4", "c5")
+            r2 = bench_step(w2, 10 if b2 else 100, 2 if b2 else 10, per_group=False)
+            if r2["timed_out"]:
+                print(f"a skinny-path wait timed out in {key}: the results are invalid", file=sys.stderr)
+                return 3
+            r2["steps"] = 10 if b2 else 100
+            extra[key] = {**_summary(w2, r2), "roofline": _roofline(w2, r2)}
+        out["others"] = extra
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl if not big else WL.custom([wl.shapes[0]], dtype=wl.dtype,
-                                                                        g_std=wl.g_std, number=wl.number),
-                                           args.cpu_seconds)
+        if big:
+            # one matrix of each shape group, one step each, extrapolated
+            keys = []
+            for sh in wl.shapes:
+                k = (min(sh[-2:]), max(sh[-2:]))
+                if k not in [x[0] for x in keys]:
+                    keys.append((k, sh))
+            sample = WL.custom([sh for _, sh in keys], dtype=wl.dtype, g_std=wl.g_std, number=wl.number)
+            out["cpu_baseline"] = cpu_baseline(sample, args.cpu_seconds)
+            out["cpu_baseline"]["sample"] += " (one matrix per shape group; the rate extrapolates to the set)"
+        else:
+            out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -276,6 +276,21 @@ muon_status muon_workspace_status(muon_plan plan, void* workspace, size_t worksp
  * default).  Meant for tests of the timeout path. */
 void muon_set_wait_limit(uint32_t polls);
 
+/* ---- Kernel timing for benchmarks ----------------------------------------
+ * While enabled, every apply of the MFMA path (X' = P X or R X: the largest
+ * launch of a large-matrix step, with its partial-round launch if any) is
+ * bracketed by a pair of HIP events recorded on the launch stream, up to
+ * 4096 applies between two reads.  Off by default; process-wide; not for use
+ * while another host thread steps.  Enabling creates the events once. */
+muon_status muon_kernel_timing(int32_t enable);
+
+/* Waits for the recorded events and returns, over the applies recorded since
+ * the last read: their summed duration in ms, their number, their algorithmic
+ * flops (2 m^2 n per matrix: one m x m by m x n product) and the MFMA flops
+ * they executed (one product per pair of operand planes: 2, 3 or 4 of them
+ * with lo planes).  Resets the totals. */
+muon_status muon_kernel_timing_read(double* ms, int64_t* launches, double* alg_flops, double* exec_flops);
+
 const char* muon_status_str(muon_status s);
 const char* muon_last_error_detail(void);
 

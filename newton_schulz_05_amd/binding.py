@@ -35,6 +35,7 @@ EXPORTS = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes",
            "muon_plan_num_groups", "muon_plan_group_info", "muon_step", "muon_ns",
            "muon_plan_num_matrices", "muon_plan_assign", "muon_shard_update", "muon_adamw_step",
            "muon_workspace_status", "muon_set_wait_limit", "muon_poll_timeout", "muon_step_noalloc",
+           "muon_kernel_timing", "muon_kernel_timing_read",
            "muon_status_str", "muon_last_error_detail", "muon_version"]
 
 
@@ -100,6 +101,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_set_wait_limit.restype = None
     lib.muon_poll_timeout.argtypes = [P(i32)]
     lib.muon_poll_timeout.restype = i32
+    lib.muon_kernel_timing.argtypes = [i32]
+    lib.muon_kernel_timing.restype = i32
+    lib.muon_kernel_timing_read.argtypes = [P(ctypes.c_double), P(i64), P(ctypes.c_double), P(ctypes.c_double)]
+    lib.muon_kernel_timing_read.restype = i32
     lib.muon_status_str.argtypes = [i32]
     lib.muon_status_str.restype = ctypes.c_char_p
     lib.muon_last_error_detail.argtypes = []
@@ -410,6 +415,21 @@ def poll_timeout() -> bool:
     flag = ctypes.c_int32()
     _check(load_library().muon_poll_timeout(ctypes.byref(flag)))
     return bool(flag.value)
+
+
+def kernel_timing(enable: bool) -> None:
+    """Start or stop event timing of the MFMA path's apply launches
+    (muon_kernel_timing); for benchmarks."""
+    _check(load_library().muon_kernel_timing(1 if enable else 0))
+
+
+def kernel_timing_read() -> dict:
+    """Summed duration (ms), count, algorithmic and executed flops of the
+    applies timed since the last read (muon_kernel_timing_read)."""
+    ms, n, alg, ex = ctypes.c_double(), ctypes.c_int64(), ctypes.c_double(), ctypes.c_double()
+    _check(load_library().muon_kernel_timing_read(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(alg),
+                                                  ctypes.byref(ex)))
+    return dict(ms=ms.value, launches=int(n.value), alg_flops=alg.value, exec_flops=ex.value)
 
 
 def set_wait_limit(polls: int) -> None:

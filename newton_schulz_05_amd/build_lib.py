@@ -23,7 +23,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-Wno-unused-variable"] + DEVICE_FLAGS
 
-SOURCES = ["plan.cpp", "validate.cpp", "api.cpp", "k_large.hip", "k_skinny.hip", "k_elem.hip"]
+SOURCES = ["plan.cpp", "validate.cpp", "api.cpp", "timer.cpp", "k_large.hip", "k_skinny.hip", "k_elem.hip"]
 
 
 def _compile(src: str) -> str:
@@ -37,7 +37,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(7, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]

@@ -153,6 +153,7 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         a.epoch = 0;
         a.epoch_dev = nullptr;
         a.host_flag = dev.host_flag;
+        a.lobuf = ws + P.ws_dyn_off + skinny_lo_offset(grp, ch.count);
         if (cap) {
           uint32_t* counter = a.sync + muon::kSyncEpochWord;
           e = muon::run_epoch_bump(counter, st);
@@ -174,7 +175,9 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         a.np = grp.np;
         a.tile = grp.tile;
         a.bf16 = (grp.path == PATH_MFMA);
-        a.grouped = grp.grouped;
+        a.whole = grp.whole;
+        a.precise = grp.precise;
+        a.x0_lo = a.bf16 && sc.mode == 0;  // muon_ns inputs are bf16 already: no lo part
         a.cus = dev.cus;
         e = run_large(a, st);
       }
@@ -443,6 +446,19 @@ muon_status muon_ns(muon_plan plan, const void* const* in_ptrs, float* const* ou
   if (s != MUON_OK) return fail(s, d);
   muon::StepScalars sc{0.f, 0.f, 0.f, 1.f, a, b, c, 0, ns_steps, 1};
   return enqueue(*P, (void* const*)out_ptrs, in_ptrs, nullptr, sc, workspace, (hipStream_t)stream);
+}
+
+muon_status muon_kernel_timing(int32_t enable) {
+  if (hipError_t e = muon::timer_enable(enable != 0); e != hipSuccess)
+    return fail(MUON_ERR_HIP, std::string("creating timing events failed: ") + hipGetErrorString(e));
+  return MUON_OK;
+}
+
+muon_status muon_kernel_timing_read(double* ms, int64_t* launches, double* alg_flops, double* exec_flops) {
+  if (!ms || !launches || !alg_flops || !exec_flops) return fail(MUON_ERR_INVALID_ARG, "null output pointer");
+  if (hipError_t e = muon::timer_read(ms, launches, alg_flops, exec_flops); e != hipSuccess)
+    return fail(MUON_ERR_HIP, std::string("reading timing events failed: ") + hipGetErrorString(e));
+  return MUON_OK;
 }
 
 const char* muon_status_str(muon_status s) {

@@ -39,10 +39,14 @@ namespace muon {
 // with them the order in which norm_kernel adds them, depend on the stored
 // shape alone and not on the padding (which follows the GEMM tile, and so
 // the group the matrix is in).  Tiles of padding only write no slot.
+// With Xl and Xtl (bf16 muon_step), U is also split into hi + lo bf16
+// planes, U ~ hi + lo to about 16 mantissa bits: X and Xt get hi, Xl and Xtl
+// get lo = bf16(U - hi).
 template <typename PT, typename XT>
 __global__ __launch_bounds__(256) void momentum_kernel(MatTable tab, StepScalars sc, int tilesR,
                                                        int tilesC, XT* __restrict__ X,
-                                                       XT* __restrict__ Xt0, int64_t xstride,
+                                                       XT* __restrict__ Xt0, XT* __restrict__ Xl,
+                                                       XT* __restrict__ Xtl, int64_t xstride,
                                                        int64_t mp, int64_t np, int64_t m,
                                                        int64_t n, float* __restrict__ normpart,
                                                        int64_t tiles) {
@@ -63,6 +67,9 @@ __global__ __launch_bounds__(256) void momentum_kernel(MatTable tab, StepScalars
   float* M = tab.e[z].m;
   XT* nat = (tr ? Xt0 : X) + int64_t(z) * xstride;  // same orientation as the stored matrix
   XT* trn = (tr ? X : Xt0) + int64_t(z) * xstride;  // transposed
+  const bool lo = Xl != nullptr;
+  XT* natl = lo ? (tr ? Xtl : Xl) + int64_t(z) * xstride : nullptr;
+  XT* trnl = lo ? (tr ? Xl : Xtl) + int64_t(z) * xstride : nullptr;
   const int64_t ldn = colsP, ldt = rowsP;
   float ss = 0.f;
   // Vector path (bf16, tile inside the matrix, 16-byte aligned rows): thread
@@ -93,17 +100,34 @@ __global__ __launch_bounds__(256) void momentum_kernel(MatTable tab, StepScalars
 #pragma unroll
         for (int d = 0; d < 4; ++d) xw[d] = f2bf2(u[2 * d], u[2 * d + 1]);
         *(u32x4*)(nat + (r0 + lr) * ldn + c0 + 8 * cgrp) = xw;
+        if (lo) {
+          u32x4 lw;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) tileT[lr][8 * cgrp + k] = bf2f(uint16_t((k & 1) ? (xw[k >> 1] >> 16) : (xw[k >> 1] & 0xffffu)));
+          for (int d = 0; d < 4; ++d)
+            lw[d] = f2bf2(u[2 * d] - bf2f(uint16_t(xw[d] & 0xffffu)), u[2 * d + 1] - bf2f(uint16_t(xw[d] >> 16)));
+          *(u32x4*)(natl + (r0 + lr) * ldn + c0 + 8 * cgrp) = lw;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tileT[lr][8 * cgrp + k] = u[k];
       }
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int lc = rr + 32 * q;
+        float uv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) uv[k] = tileT[8 * cgrp + k][lc];
         u32x4 tw;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) tw[d] = f2bf2(tileT[8 * cgrp + 2 * d][lc], tileT[8 * cgrp + 2 * d + 1][lc]);
+        for (int d = 0; d < 4; ++d) tw[d] = f2bf2(uv[2 * d], uv[2 * d + 1]);
         *(u32x4*)(trn + (c0 + lc) * ldt + r0 + 8 * cgrp) = tw;
+        if (lo) {
+          u32x4 lw;
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            lw[d] = f2bf2(uv[2 * d] - bf2f(uint16_t(tw[d] & 0xffffu)), uv[2 * d + 1] - bf2f(uint16_t(tw[d] >> 16)));
+          *(u32x4*)(trnl + (c0 + lc) * ldt + r0 + 8 * cgrp) = lw;
+        }
       }
       const float tot = block_sum_256(ss, red);
       if (t == 0) normpart[int64_t(z) * tiles + slot] = tot;
@@ -134,9 +158,11 @@ __global__ __launch_bounds__(256) void momentum_kernel(MatTable tab, StepScalars
       // the value stored is what NS consumes (rounded to the storage type)
       XT xv;
       Elem<XT>::store(&xv, u);
-      const float ur = Elem<XT>::load(&xv);
-      if (r < rowsP && c < colsP) nat[r * ldn + c] = xv;
-      tileT[lr][lc] = ur;
+      if (r < rowsP && c < colsP) {
+        nat[r * ldn + c] = xv;
+        if (lo) Elem<XT>::store(natl + r * ldn + c, u - Elem<XT>::load(&xv));
+      }
+      tileT[lr][lc] = u;
     }
   }
   __syncthreads();
@@ -151,8 +177,10 @@ __global__ __launch_bounds__(256) void momentum_kernel(MatTable tab, StepScalars
       const int64_t r = r0 + lr;
       if (c < colsP && r < rowsP) {
         XT xv;
-        Elem<XT>::store(&xv, tileT[lr][lc]);
+        const float u = tileT[lr][lc];
+        Elem<XT>::store(&xv, u);
         trn[c * ldt + r] = xv;
+        if (lo) Elem<XT>::store(trnl + c * ldt + r, u - Elem<XT>::load(&xv));
       }
     }
   }
@@ -319,9 +347,9 @@ struct EpiGramBf16 {
 };
 
 // Poly (bf16 path): P = ps*(a I + b A + c S); off-diagonal bf16 (mirrored),
-// diagonal fp32 in Pd
+// with its lo part bf16(P - hi) in PoffL when given, diagonal fp32 in Pd
 struct EpiPolyBf16 {
-  const float* A; uint16_t* Poff; float* Pd; const float* scal; int use_scale;
+  const float* A; uint16_t* Poff; uint16_t* PoffL; float* Pd; const float* scal; int use_scale;
   float a, b, c; int64_t mp, m;
   static constexpr bool kCol = true;
   __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool diag) const {
@@ -344,10 +372,23 @@ struct EpiPolyBf16 {
       v[k] = p;
     }
     Seg<uint16_t>::store(Poff + o, k0, 16, pv);
+    if (PoffL) {
+      float lo[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) lo[k] = pv[k] - bf2f(f2bf(pv[k]));
+      Seg<uint16_t>::store(PoffL + o, k0, 16, lo);
+    }
   }
   __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
     const int k1 = diag ? clamp16(j - i0) : 16;
-    Seg<uint16_t>::store(Poff + int64_t(z) * mp * mp + j * mp + i0, 0, k1, v);
+    const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
+    Seg<uint16_t>::store(Poff + o, 0, k1, v);
+    if (PoffL) {
+      float lo[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
+      Seg<uint16_t>::store(PoffL + o, 0, k1, lo);
+    }
   }
 };
 
@@ -390,12 +431,15 @@ struct EpiSymMul {
 
 // Grouped steps: R = ps * F1 F0 for two commuting symmetric factors stored as
 // off-diagonal bf16 plus fp32 diagonal (F0 = Poff0 + diag(Pd0), the same for
-// F1): acc = Poff1 Poff0^T from the GEMM, plus Pd1[i] Poff0[i][j] +
+// F1; with lo planes Poff0L / Poff1L the off-diagonals are hi + lo):
+// acc = Poff1 Poff0^T from the GEMM, plus Pd1[i] Poff0[i][j] +
 // Poff1[i][j] Pd0[j] + [i == j] Pd1[i] Pd0[i].  Off-diagonal R in bf16
-// (mirrored), diagonal in fp32, the layout the apply and the next R take.
+// (mirrored; its lo part in RoffL when given), diagonal in fp32, the layout
+// the apply and the next R take.
 struct EpiPairR {
-  const uint16_t* Poff0; const float* Pd0; const uint16_t* Poff1; const float* Pd1;
-  uint16_t* Roff; float* Rd; const float* scal; int use_scale; int64_t mp;
+  const uint16_t* Poff0; const uint16_t* Poff0L; const float* Pd0;
+  const uint16_t* Poff1; const uint16_t* Poff1L; const float* Pd1;
+  uint16_t* Roff; uint16_t* RoffL; float* Rd; const float* scal; int use_scale; int64_t mp;
   static constexpr bool kCol = true;
   __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool diag) const {
     const float ps = use_scale ? scal[z * 4 + 0] : 1.0f;
@@ -404,6 +448,18 @@ struct EpiPairR {
     float p0[16] = {}, p1[16] = {}, d0[16] = {}, rv[16];
     Seg<uint16_t>::load(Poff0 + o, k0, 16, p0);
     Seg<uint16_t>::load(Poff1 + o, k0, 16, p1);
+    if (Poff0L) {
+      float l[16] = {};
+      Seg<uint16_t>::load(Poff0L + o, k0, 16, l);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) p0[k] += l[k];
+    }
+    if (Poff1L) {
+      float l[16] = {};
+      Seg<uint16_t>::load(Poff1L + o, k0, 16, l);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) p1[k] += l[k];
+    }
     Seg<float>::load(Pd0 + int64_t(z) * mp + j0, k0, 16, d0);
     const float d1 = Pd1[int64_t(z) * mp + i];
 #pragma unroll
@@ -420,24 +476,44 @@ struct EpiPairR {
       v[k] = r;
     }
     Seg<uint16_t>::store(Roff + o, k0, 16, rv);
+    if (RoffL) {
+      float lo[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) lo[k] = rv[k] - bf2f(f2bf(rv[k]));
+      Seg<uint16_t>::store(RoffL + o, k0, 16, lo);
+    }
   }
   __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
     const int k1 = diag ? clamp16(j - i0) : 16;
-    Seg<uint16_t>::store(Roff + int64_t(z) * mp * mp + j * mp + i0, 0, k1, v);
+    const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
+    Seg<uint16_t>::store(Roff + o, 0, k1, v);
+    if (RoffL) {
+      float lo[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
+      Seg<uint16_t>::store(RoffL + o, 0, k1, lo);
+    }
   }
 };
 
-// Apply (bf16 path): X' = acc + Pd[i] * X[i][j]; X' and X'^T in bf16, or on
-// the last step the weight update (O) at the stored position
+// Apply (bf16 path): X' = acc + Pd[i] * X[i][j] (X = hi + lo when Xl is
+// given); X' and X'^T in bf16, or on the last step the weight update (O) at
+// the stored position
 template <typename PT>
 struct EpiApplyBf16 {
-  MatTable tab; StepScalars sc; uint16_t* X; uint16_t* XtN; const float* Pd;
+  MatTable tab; StepScalars sc; uint16_t* X; const uint16_t* Xl; uint16_t* XtN; const float* Pd;
   int64_t mp, np, m, n; int last;
   static constexpr bool kCol = true;
   __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool) const {
     uint16_t* Xr = X + int64_t(z) * mp * np + i * np + j0;
     float x[16];
     Seg<uint16_t>::load(Xr, 0, 16, x);
+    if (Xl) {
+      float l[16];
+      Seg<uint16_t>::load(Xl + int64_t(z) * mp * np + i * np + j0, 0, 16, l);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) x[k] += l[k];
+    }
     const float d = Pd[int64_t(z) * mp + i];
 #pragma unroll
     for (int k = 0; k < 16; ++k) v[k] = fmaf(d, x[k], v[k]);
@@ -531,13 +607,15 @@ __device__ __forceinline__ void tile_coords(int t, int T, bool upper, int& ti, i
 // chunks per instruction) hit distinct banks:
 //   BK = 64 (8 chunks a row): g(r) = (r & 7) ^ ((r >> 3) & 3)
 //   BK = 32 (4 chunks a row): g(r) = ((r >> 1) ^ (r >> 3)) & 3
-// NPROD = 1: C = A B^T (BK = 64).
-// NPROD = 3: C = Ah Bh^T + Ah Bl^T + Al Bh^T (four operand planes, BK = 32,
-//            so the LDS footprint matches).
-// Per 16-wide k slice every output element takes its MFMA products in the
-// same order whatever TILE is, and zero padding adds exact zeros, so the two
-// tile sizes give bitwise identical results.
-// ============================================================================
+// PR selects the products (operands given as bf16 hi planes Ah, Bh and, for
+// the split products, lo planes Al, Bl with A ~ Ah + Al, B ~ Bh + Bl):
+//   kHH = 1: Ah Bh^T       kHL = 2: Ah Bl^T       kLH = 4: Al Bh^T
+// always with kHH; per k slice the products are taken in the order HH, HL,
+// LH.  One plane per side (PR = kHH) uses BK = 64; with a lo plane on either
+// side BK = 32, so the LDS footprint of the three or four planes stays within
+// that of two at BK = 64.
+constexpr int kHH = 1, kHL = 2, kLH = 4;
+
 template <int TILE>
 struct GemmGeom {
   static constexpr int NT = (TILE == 256) ? 512 : 256;
@@ -560,20 +638,22 @@ __device__ __forceinline__ int chunk_swz(int row) {
   else return ((row >> 1) ^ (row >> 3)) & 3;
 }
 
-template <int TILE, int NPROD, typename Epi>
+template <int TILE, int PR, typename Epi>
 __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void gemm_bf16_kernel(
     const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al, int64_t lda, int64_t sA,
     const uint16_t* __restrict__ Bh, const uint16_t* __restrict__ Bl, int64_t ldb, int64_t sB,
     int64_t K, int tilesN, int upper, int per, int base, int split, Epi epi) {
   using G = GemmGeom<TILE>;
-  constexpr int NA = (NPROD == 3) ? 2 : 1;      // operand planes per side
-  constexpr int BK = (NPROD == 3) ? 32 : 64;
+  constexpr int NA = (PR & kLH) ? 2 : 1;        // A planes
+  constexpr int NB = (PR & kHL) ? 2 : 1;        // B planes
+  constexpr int NPL = NA + NB;
+  constexpr int BK = (NPL > 2) ? 32 : 64;
   constexpr int CPR = BK / 8;                   // 16-byte chunks per row
   constexpr int PLANE = TILE * CPR;             // chunks per operand plane
   constexpr int NW = G::NT / 64;
   constexpr int LP = PLANE / G::NT;             // loads per thread per plane
   constexpr int KS = BK / 16;
-  __shared__ u16x8 lds[2][2 * NA][PLANE];       // [stage][Ah, (Al), Bh, (Bl)]
+  __shared__ u16x8 lds[2][NPL][PLANE];          // [stage][Ah, (Al), Bh, (Bl)]
   // Work item f = matrix * per + tile, in units of the tiles that tilesN
   // counts.  With split, each such tile (twice TILE on a side) is done by four
   // workgroups, one per TILE-quarter; a symmetric output skips the quarter
@@ -592,13 +672,11 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int wr = (wv / G::WN) * G::TMW, wc = (wv % G::WN) * G::TNW;
 
-  const uint16_t* gsrc[2 * NA];
+  const uint16_t* gsrc[NPL];
   gsrc[0] = Ah + int64_t(z) * sA + row0 * lda;
   gsrc[NA] = Bh + int64_t(z) * sB + col0 * ldb;
-  if constexpr (NA == 2) {
-    gsrc[1] = Al + int64_t(z) * sA + row0 * lda;
-    gsrc[3] = Bl + int64_t(z) * sB + col0 * ldb;
-  }
+  if constexpr (NA == 2) gsrc[1] = Al + int64_t(z) * sA + row0 * lda;
+  if constexpr (NB == 2) gsrc[NA + 1] = Bl + int64_t(z) * sB + col0 * ldb;
 
   f32x16 acc[G::FM][G::FN];
 #pragma unroll
@@ -611,7 +689,7 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
   // c % CPR, which holds logical chunk (c % CPR) ^ g(row)
   auto gload = [&](int64_t k0, int st) {
 #pragma unroll
-    for (int s = 0; s < 2 * NA; ++s) {
+    for (int s = 0; s < NPL; ++s) {
       const int64_t ld = (s < NA) ? lda : ldb;
 #pragma unroll
       for (int p = 0; p < LP; ++p) {
@@ -621,7 +699,7 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
       }
     }
   };
-  bf16x8 fa[2][NA][G::FM], fb[2][NA][G::FN];
+  bf16x8 fa[2][NA][G::FM], fb[2][NB][G::FN];
   auto lread = [&](int st, int ks, int buf) {
     const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
@@ -631,6 +709,9 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
         const int r = wr + x * 32 + (lane & 31);
         fa[buf][s][x] = as_bf16x8(lds[st][s][r * CPR + (ch ^ chunk_swz<CPR>(r))]);
       }
+    }
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
 #pragma unroll
       for (int x = 0; x < G::FN; ++x) {
         const int r = wc + x * 32 + (lane & 31);
@@ -649,10 +730,8 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
 #pragma unroll
         for (int b = 0; b < G::FN; ++b) {
           acc[a][b] = mfma32x32x16(fa[q][0][a], fb[q][0][b], acc[a][b]);
-          if constexpr (NPROD == 3) {
-            acc[a][b] = mfma32x32x16(fa[q][0][a], fb[q][NA - 1][b], acc[a][b]);
-            acc[a][b] = mfma32x32x16(fa[q][NA - 1][a], fb[q][0][b], acc[a][b]);
-          }
+          if constexpr ((PR & kHL) != 0) acc[a][b] = mfma32x32x16(fa[q][0][a], fb[q][NB - 1][b], acc[a][b]);
+          if constexpr ((PR & kLH) != 0) acc[a][b] = mfma32x32x16(fa[q][NA - 1][a], fb[q][0][b], acc[a][b]);
         }
     }
   };
@@ -757,15 +836,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // ============================================================================
 template <typename PT, typename XT>
 __global__ __launch_bounds__(256) void ns0_kernel(MatTable tab, StepScalars sc, const XT* __restrict__ X,
-                                                  int64_t mp, int64_t np, int64_t m, int64_t n,
-                                                  const float* __restrict__ scal) {
+                                                  const XT* __restrict__ Xl, int64_t mp, int64_t np, int64_t m,
+                                                  int64_t n, const float* __restrict__ scal) {
   const int z = blockIdx.y;
   const bool tr = tab.tr[z] != 0;
   const float s = scal[z * 4 + 0];
   const XT* Xz = X + int64_t(z) * mp * np;
   for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < m * n; e += int64_t(gridDim.x) * 256) {
     const int64_t i = e / n, j = e % n;
-    NatStore::put<PT>(tab.e[z], sc, tr, m, n, i, j, s * Elem<XT>::load(Xz + i * np + j));
+    float u = Elem<XT>::load(Xz + i * np + j);
+    if (Xl) u += Elem<XT>::load(Xl + int64_t(z) * mp * np + i * np + j);
+    NatStore::put<PT>(tab.e[z], sc, tr, m, n, i, j, s * u);
   }
 }
 
@@ -780,19 +861,19 @@ static hipError_t last_launch() { return hipGetLastError(); }
 // workgroups per tile (three on the diagonal of a symmetric output), so that
 // round costs a fraction of a full one on an otherwise idle chip.  Tile size
 // changes no bit of the result.
-template <int TILE, int NPROD, typename Epi>
+template <int TILE, int PR, typename Epi>
 static hipError_t gemm_launch(const uint16_t* Ah, const uint16_t* Al, int64_t lda, int64_t sA, const uint16_t* Bh,
                               const uint16_t* Bl, int64_t ldb, int64_t sB, int64_t K, int tilesN, int upper, int per,
                               int count, int cus, const Epi& epi, hipStream_t st) {
   const int total = per * count;
   const int round = cus * GemmGeom<TILE>::PER_CU;
   const int main = (cus > 0 && total > round) ? total - total % round : total;
-  hipLaunchKernelGGL((gemm_bf16_kernel<TILE, NPROD, Epi>), dim3(unsigned(main)), dim3(GemmGeom<TILE>::NT), 0, st,
+  hipLaunchKernelGGL((gemm_bf16_kernel<TILE, PR, Epi>), dim3(unsigned(main)), dim3(GemmGeom<TILE>::NT), 0, st,
                      Ah, Al, lda, sA, Bh, Bl, ldb, sB, K, tilesN, upper, per, 0, 0, epi);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (main == total) return hipSuccess;
   constexpr int SUB = TILE / 2;
-  hipLaunchKernelGGL((gemm_bf16_kernel<SUB, NPROD, Epi>), dim3(unsigned(4 * (total - main))),
+  hipLaunchKernelGGL((gemm_bf16_kernel<SUB, PR, Epi>), dim3(unsigned(4 * (total - main))),
                      dim3(GemmGeom<SUB>::NT), 0, st, Ah, Al, lda, sA, Bh, Bl, ldb, sB, K, tilesN, upper, per, main, 1,
                      epi);
   return hipGetLastError();
@@ -820,133 +901,152 @@ static inline bool split_a2(int64_t m, int k, int steps) {
   return m < kPlainMinM || k >= std::min(kPlainSteps, steps - 2);
 }
 
-// One NS step of the bf16 path: Gram, poly, apply.
-template <int TILE, typename PT>
-static hipError_t ns_step_bf16(const LargeArgs& g, hipStream_t st, int k, int cur, int last) {
-  const LargeLayout& L = g.L;
-  uint8_t* ws = (uint8_t*)g.ws;
-  uint16_t* X = (uint16_t*)(ws + L.x);
-  uint16_t* Xt[2] = {(uint16_t*)(ws + L.xt0), (uint16_t*)(ws + L.xt1)};
-  float* A = (float*)(ws + L.a);
-  float* scal = (float*)(ws + L.scal);
-  uint16_t* H = (uint16_t*)(ws + L.h);
-  uint16_t* Lo = (uint16_t*)(ws + L.l);
-  uint16_t* Poff = (uint16_t*)(ws + L.poff);
-  float* Pd = (float*)(ws + L.pdiag);
-  const int64_t mp = g.mp, np = g.np;
-  if (mp % TILE != 0 || np % TILE != 0) return hipErrorInvalidValue;
-  const int Tm = int(mp / TILE), Tn = int(np / TILE);
-  const unsigned up = unsigned(Tm * (Tm + 1) / 2);
-  const bool split = split_a2(g.m, k, g.sc.ns_steps);
-  // Gram: upper tiles of [mp x mp], K = np
-  EpiGramBf16 eg{A, H, Lo, scal, k == 0, split ? 1 : 0, mp};
-  if (hipError_t e = gemm_launch<TILE, 1>(X, nullptr, np, L.x_stride, X, nullptr, np, L.x_stride, np, Tm, 1, int(up),
-                                          g.count, g.cus, eg, st);
-      e != hipSuccess)
-    return e;
-  // Poly: S = HH + HL + LH (split steps) or S = HH over upper tiles, K = mp
-  EpiPolyBf16 ep{A, Poff, Pd, scal, k == 0, g.sc.a, g.sc.b, g.sc.c, mp, g.m};
-  if (hipError_t e = split ? gemm_launch<TILE, 3>(H, Lo, mp, L.a_stride, H, Lo, mp, L.a_stride, mp, Tm, 1, int(up),
-                                                  g.count, g.cus, ep, st)
-                           : gemm_launch<TILE, 1>(H, nullptr, mp, L.a_stride, H, nullptr, mp, L.a_stride, mp, Tm, 1,
-                                                  int(up), g.count, g.cus, ep, st);
-      e != hipSuccess)
-    return e;
-  // Apply: X' = Poff Xt^T + diag(Pd) X, K = mp
-  EpiApplyBf16<PT> ea{g.tab, g.sc, X, Xt[cur ^ 1], Pd, mp, np, g.m, g.n, last};
-  return gemm_launch<TILE, 1>(Poff, nullptr, mp, L.a_stride, Xt[cur], nullptr, mp, L.x_stride, mp, Tn, 0, Tm * Tn,
-                              g.count, g.cus, ea, st);
-}
-
-// Steps of a group (bf16 path, wide groups): G >= 2 consecutive NS steps
-// k .. k+G-1 with one Gram and one apply.  Every P_j, A_j and product below is
-// a polynomial in A_k, so they commute and the products are symmetric (upper
-// tiles, mirrored).  For j = 0 .. G-1:
+// A group of G >= 1 consecutive NS steps k .. k+G-1 of the bf16 path, with
+// one Gram and one apply.  Every P_j, A_j and product below is a polynomial
+// in A_k, so they commute and the products are symmetric (upper tiles,
+// mirrored).  For j = 0 .. G-1:
 //   j = 0   Gram  A_0 = sc X X^T                  -> A fp32 (upper), H (+ L)
-//           poly  P_0 = a I + b A_0 + c A_0^2     -> Pb[0] (no scale s)
-//   j >= 1  T     T = P_{j-1} A_{j-1}             -> fp32 over A, Th
+//           poly  P_0 = a I + b A_0 + c A_0^2     -> Pb[0] (scaled by s only
+//                 when G = 1 and k = 0)
+//   j >= 1  T     T = P_{j-1} A_{j-1}             -> fp32 over A, Th (+ Tl)
 //           A'    A_j = P_{j-1} T                 -> fp32 over A, H (+ L)
 //           poly  P_j from A_j                    -> Pb[j % 2]
 //           R     R_j = P_j R_{j-1}, R_0 = s P_0  -> Rb[j % 2] (off-diagonal
 //                 bf16, diagonal fp32; s only when k = 0)
-//   apply   X_{k+G} = Roff Xt^T + diag(Rd) X, R = R_{G-1}
+//   apply   X_{k+G} = Roff Xt^T + diag(Rd) X with R = R_{G-1} (P_0 when G = 1)
 // A_j = X_{k+j} X_{k+j}^T in exact arithmetic, so this is the oracle's
 // iteration with one m x n product pair per group.
 //
-// Which steps are grouped (group_len): the first min(4, N - 1) steps of N
-// form one group, and the rest go in pairs with a single step last when odd
-// (N = 5: 4 + 1; 6: 4 + 2; 7: 4 + 2 + 1; 2: one pair).  In an emulation of
-// these roundings (quintic coefficients) this order was the most accurate of
-// those tried: early steps, whose normalised singular values are small and
-// whose P is near a I, lose nothing in the m x m space, while the last steps
-// need A from a fresh Gram of X.  At 1024 x 3584 with 5 steps the relative
-// Frobenius error of O was 4.2e-3 for single steps and 3.2e-3 grouped on
-// Gaussian inputs, 1.9e-2 and 6.4e-3 with singular values spread over
-// [1e-2, 1], 3.0e-2 and 8.1e-3 over [1e-3, 1]; one group of all 5 steps gave
-// 2.7e-3, 3.0e-2 and 4.7e-2.
+// Precision.  An error made in an early NS step in the direction of a small
+// singular value is multiplied by up to a = 3.4445 in every later step, so
+// ill-conditioned inputs (such as momenta, whose spectra spread over
+// decades) need the early iterates to more than bf16 precision.  Hence:
+//   - in muon_step, X_0 = U carries its lo plane (U ~ hi + lo to about 16
+//     mantissa bits), used by the first apply (products kHH + kHL and the
+//     diagonal term) and, in the precise recipe, by the first Gram;
+//   - the first group spans the first min(4, N - 1) steps (all N when the
+//     recipe takes them whole), so X is rounded to bf16 only after the
+//     steps whose errors would be multiplied most;
+//   - the precise recipe (m < kLeanFromM, or more than kLeanMaxSteps steps)
+//     also splits the m x m chain: P, T and R carry lo planes and T, A' and
+//     R take the split products, and the apply uses the lo plane of R.
+// See ns_recipe (plan.cpp) for which shapes take which recipe.
 template <int TILE, typename PT>
 static hipError_t ns_group_bf16(const LargeArgs& g, hipStream_t st, int k, int G, int cur, int last) {
   const LargeLayout& L = g.L;
   uint8_t* ws = (uint8_t*)g.ws;
   uint16_t* X = (uint16_t*)(ws + L.x);
   uint16_t* Xt[2] = {(uint16_t*)(ws + L.xt0), (uint16_t*)(ws + L.xt1)};
+  uint16_t* Xl = (uint16_t*)(ws + L.xl);
+  uint16_t* Xtl = (uint16_t*)(ws + L.xtl);
   float* A = (float*)(ws + L.a);
   float* scal = (float*)(ws + L.scal);
   uint16_t* H = (uint16_t*)(ws + L.h);
   uint16_t* Lo = (uint16_t*)(ws + L.l);
   uint16_t* Th = (uint16_t*)(ws + L.th);
+  // the lean recipe holds up to kLeanMaxSteps steps; beyond, the precise chain
+  const bool cs = g.precise || g.sc.ns_steps > kLeanMaxSteps;
+  uint16_t* Tl = cs ? (uint16_t*)(ws + L.tl) : nullptr;
   uint16_t* Pb[2] = {(uint16_t*)(ws + L.poff), (uint16_t*)(ws + L.poff2)};
+  uint16_t* PbL[2] = {cs ? (uint16_t*)(ws + L.poffl0) : nullptr, cs ? (uint16_t*)(ws + L.poffl1) : nullptr};
   float* Pdb[2] = {(float*)(ws + L.pdiag), (float*)(ws + L.pdiag2)};
   uint16_t* Rb[2] = {(uint16_t*)(ws + L.roff0), (uint16_t*)(ws + L.roff1)};
+  uint16_t* RbL[2] = {cs ? (uint16_t*)(ws + L.roffl0) : nullptr, cs ? (uint16_t*)(ws + L.roffl1) : nullptr};
   float* Rdb[2] = {(float*)(ws + L.rdiag0), (float*)(ws + L.rdiag1)};
   const int64_t mp = g.mp, np = g.np;
-  if (mp % TILE != 0 || np % TILE != 0 || !g.grouped || G < 2) return hipErrorInvalidValue;
+  if (mp % TILE != 0 || np % TILE != 0 || G < 1) return hipErrorInvalidValue;
   const int Tm = int(mp / TILE), Tn = int(np / TILE);
   const int up = Tm * (Tm + 1) / 2;
   const int steps = g.sc.ns_steps;
+  const bool xlo = (k == 0) && g.x0_lo;       // X_0 = U carries its lo plane
+  const int64_t as = L.a_stride, xs = L.x_stride;
   hipError_t e;
-  auto poly = [&](int j) {
-    const bool split = split_a2(g.m, k + j, steps);
-    EpiPolyBf16 ep{A, Pb[j & 1], Pdb[j & 1], scal, 0, g.sc.a, g.sc.b, g.sc.c, mp, g.m};
-    return split ? gemm_launch<TILE, 3>(H, Lo, mp, L.a_stride, H, Lo, mp, L.a_stride, mp, Tm, 1, up, g.count,
-                                        g.cus, ep, st)
-                 : gemm_launch<TILE, 1>(H, nullptr, mp, L.a_stride, H, nullptr, mp, L.a_stride, mp, Tm, 1, up,
-                                        g.count, g.cus, ep, st);
+  // symmetric m x m product launches: C = Ah Bh^T (+ split products)
+  auto sym1 = [&](const uint16_t* a, const uint16_t* b, const auto& epi) {
+    return gemm_launch<TILE, kHH>(a, nullptr, mp, as, b, nullptr, mp, as, mp, Tm, 1, up, g.count, g.cus, epi, st);
   };
-  EpiGramBf16 eg{A, H, Lo, scal, k == 0, split_a2(g.m, k, steps) ? 1 : 0, mp};
-  if ((e = gemm_launch<TILE, 1>(X, nullptr, np, L.x_stride, X, nullptr, np, L.x_stride, np, Tm, 1, up, g.count,
-                                g.cus, eg, st)) != hipSuccess)
-    return e;
+  auto sym3 = [&](const uint16_t* ah, const uint16_t* al, const uint16_t* bh, const uint16_t* bl, const auto& epi) {
+    return gemm_launch<TILE, kHH | kHL | kLH>(ah, al, mp, as, bh, bl, mp, as, mp, Tm, 1, up, g.count, g.cus, epi, st);
+  };
+  auto poly = [&](int j) {
+    const bool sp = split_a2(g.m, k + j, steps);
+    uint16_t* pl = (cs || G == 1) ? PbL[j & 1] : nullptr;
+    EpiPolyBf16 ep{A, Pb[j & 1], pl, Pdb[j & 1], scal, (G == 1 && k == 0) ? 1 : 0, g.sc.a, g.sc.b, g.sc.c, mp, g.m};
+    return sp ? sym3(H, Lo, H, Lo, ep) : sym1(H, H, ep);
+  };
+  // Gram: with X_0's lo plane in the precise recipe, X X^T ~ Xh Xh^T + Xh Xl^T + Xl Xh^T
+  EpiGramBf16 eg{A, H, Lo, scal, k == 0, (split_a2(g.m, k, steps) || cs) ? 1 : 0, mp};
+  e = (xlo && cs) ? gemm_launch<TILE, kHH | kHL | kLH>(X, Xl, np, xs, X, Xl, np, xs, np, Tm, 1, up, g.count, g.cus,
+                                                       eg, st)
+                  : gemm_launch<TILE, kHH>(X, nullptr, np, xs, X, nullptr, np, xs, np, Tm, 1, up, g.count, g.cus, eg, st);
+  if (e != hipSuccess) return e;
   if ((e = poly(0)) != hipSuccess) return e;
   for (int j = 1; j < G; ++j) {
     const int pp = (j - 1) & 1;  // P_{j-1}
-    EpiSymMul et{A, Pdb[pp], Th, nullptr, 0, mp};
-    if ((e = gemm_launch<TILE, 1>(Pb[pp], nullptr, mp, L.a_stride, H, nullptr, mp, L.a_stride, mp, Tm, 1, up,
-                                  g.count, g.cus, et, st)) != hipSuccess)
-      return e;
-    EpiSymMul ea{A, Pdb[pp], H, Lo, split_a2(g.m, k + j, steps) ? 1 : 0, mp};
-    if ((e = gemm_launch<TILE, 1>(Pb[pp], nullptr, mp, L.a_stride, Th, nullptr, mp, L.a_stride, mp, Tm, 1, up,
-                                  g.count, g.cus, ea, st)) != hipSuccess)
-      return e;
+    EpiSymMul et{A, Pdb[pp], Th, Tl, cs ? 1 : 0, mp};
+    if ((e = cs ? sym3(Pb[pp], PbL[pp], H, Lo, et) : sym1(Pb[pp], H, et)) != hipSuccess) return e;
+    EpiSymMul ea{A, Pdb[pp], H, Lo, (split_a2(g.m, k + j, steps) || cs) ? 1 : 0, mp};
+    if ((e = cs ? sym3(Pb[pp], PbL[pp], Th, Tl, ea) : sym1(Pb[pp], Th, ea)) != hipSuccess) return e;
     if ((e = poly(j)) != hipSuccess) return e;
     // R_j = P_j R_{j-1}; R_0 = s P_0 is P_0 itself with the scale applied here
     const uint16_t* r0 = (j == 1) ? Pb[0] : Rb[(j - 1) & 1];
+    const uint16_t* r0l = (j == 1) ? PbL[0] : RbL[(j - 1) & 1];
     const float* rd0 = (j == 1) ? Pdb[0] : Rdb[(j - 1) & 1];
-    EpiPairR er{r0, rd0, Pb[j & 1], Pdb[j & 1], Rb[j & 1], Rdb[j & 1], scal, (k == 0 && j == 1) ? 1 : 0, mp};
-    if ((e = gemm_launch<TILE, 1>(Pb[j & 1], nullptr, mp, L.a_stride, r0, nullptr, mp, L.a_stride, mp, Tm, 1, up,
-                                  g.count, g.cus, er, st)) != hipSuccess)
-      return e;
+    EpiPairR er{r0, cs ? r0l : nullptr, rd0, Pb[j & 1], cs ? PbL[j & 1] : nullptr, Pdb[j & 1],
+                Rb[j & 1], cs ? RbL[j & 1] : nullptr, Rdb[j & 1], scal, (k == 0 && j == 1) ? 1 : 0, mp};
+    if ((e = cs ? sym3(Pb[j & 1], PbL[j & 1], r0, r0l, er) : sym1(Pb[j & 1], r0, er)) != hipSuccess) return e;
   }
-  EpiApplyBf16<PT> eap{g.tab, g.sc, X, Xt[cur ^ 1], Rdb[(G - 1) & 1], mp, np, g.m, g.n, last};
-  return gemm_launch<TILE, 1>(Rb[(G - 1) & 1], nullptr, mp, L.a_stride, Xt[cur], nullptr, mp, L.x_stride, mp, Tn, 0,
-                              Tm * Tn, g.count, g.cus, eap, st);
+  // apply with R (P_0 for a single step): A = R (+ its lo plane, precise),
+  // B = Xt (+ X_0's lo plane)
+  const uint16_t* ra = (G == 1) ? Pb[0] : Rb[(G - 1) & 1];
+  const uint16_t* ral = (G == 1) ? PbL[0] : RbL[(G - 1) & 1];
+  const float* rd = (G == 1) ? Pdb[0] : Rdb[(G - 1) & 1];
+  EpiApplyBf16<PT> eap{g.tab, g.sc, X, xlo ? Xl : nullptr, Xt[cur ^ 1], rd, mp, np, g.m, g.n, last};
+  const uint16_t* bl = xlo ? Xtl : nullptr;
+  // algorithmic work of this apply (one m x m by m x n product per matrix)
+  // and the MFMA work it executes (one such product per operand-plane pair)
+  const double alg = 2.0 * double(g.m) * double(g.m) * double(g.n) * g.count;
+  const int prods = 1 + (xlo ? 1 : 0) + (cs ? 1 : 0);
+  timer_begin(st);
+  if (cs && xlo)
+    e = gemm_launch<TILE, kHH | kHL | kLH>(ra, ral, mp, as, Xt[cur], bl, mp, xs, mp, Tn, 0, Tm * Tn, g.count, g.cus,
+                                           eap, st);
+  else if (cs)
+    e = gemm_launch<TILE, kHH | kLH>(ra, ral, mp, as, Xt[cur], nullptr, mp, xs, mp, Tn, 0, Tm * Tn, g.count, g.cus,
+                                     eap, st);
+  else if (xlo)
+    e = gemm_launch<TILE, kHH | kHL>(ra, nullptr, mp, as, Xt[cur], bl, mp, xs, mp, Tn, 0, Tm * Tn, g.count, g.cus,
+                                     eap, st);
+  else
+    e = gemm_launch<TILE, kHH>(ra, nullptr, mp, as, Xt[cur], nullptr, mp, xs, mp, Tn, 0, Tm * Tn, g.count, g.cus,
+                               eap, st);
+  if (e != hipSuccess) return e;
+  timer_end(st, alg, alg * prods);
+  return hipSuccess;
 }
 
-// Steps taken together from step k of `steps` (grouped path): the first
-// min(4, steps - 1) (all of them when steps <= 2), then pairs, then a
-// single step when the count left is odd.
-static inline int group_len(int k, int steps) {
-  if (k == 0) return steps <= 2 ? steps : std::min(4, steps - 1);
+// Steps taken together from step k of `steps`: the first min(steps, 5) when
+// the recipe takes them whole, otherwise the first min(4, steps - 1) (all of
+// them when steps <= 2); then pairs, then a single step when the count left
+// is odd.  A longer chain A_{j+1} = P_j A_j P_j is unstable: a rounding
+// error that leaves A a slightly negative eigenvalue (A is X X^T, so none
+// exists in exact arithmetic) is multiplied by P^2, about a^2 = 11.9, in
+// every step and never brought back, which overflowed a 10-step chain of a
+// square Gaussian 300 x 300 input on the GPU.
+// In an emulation of these roundings (quintic coefficients) this order was
+// the most accurate of those tried for m >= 512: early steps, whose
+// normalised singular values are small and whose P is near a I, lose nothing
+// in the m x m space, while the last steps need A from a fresh Gram of X.
+// At 1024 x 3584 with 5 steps and no lo planes, the relative Frobenius error
+// of O was 4.2e-3 for single steps and 3.2e-3 grouped on Gaussian inputs,
+// 1.9e-2 and 6.4e-3 with singular values spread over [1e-2, 1], 3.0e-2 and
+// 8.1e-3 over [1e-3, 1]; one group of all 5 steps gave 2.7e-3, 3.0e-2 and
+// 4.7e-2 with a bf16 chain, and below 2e-3 with the split chain of the
+// precise recipe.
+constexpr int kWholeMaxSteps = 5;
+
+static inline int group_len(int k, int steps, bool whole) {
+  if (k == 0) return whole ? std::min(steps, kWholeMaxSteps) : (steps <= 2 ? steps : std::min(4, steps - 1));
   return (steps - k >= 2) ? 2 : 1;
 }
 
@@ -962,12 +1062,15 @@ static hipError_t run_large_t(const LargeArgs& g, hipStream_t st) {
   const int64_t mp = g.mp, np = g.np, m = g.m, n = g.n;
   const int count = g.count;
 
-  // momentum: 64x64 tiles over the padded matrix (64 divides mp and np)
+  // momentum: 64x64 tiles over the padded matrix (64 divides mp and np); in
+  // muon_step the bf16 NS input also gets its lo planes
+  XT* Xl = (g.x0_lo) ? (XT*)(ws + L.xl) : nullptr;
+  XT* Xtl = (g.x0_lo) ? (XT*)(ws + L.xtl) : nullptr;
   {
     const int tilesM = int(mp / 64), tilesN = int(np / 64);
     dim3 grid(unsigned(tilesM * tilesN), unsigned(count));
     hipLaunchKernelGGL((momentum_kernel<PT, XT>), grid, dim3(256), 0, st, g.tab, g.sc, tilesM,
-                       tilesN, X, Xt[0], L.x_stride, mp, np, m, n, normpart, L.tiles);
+                       tilesN, X, Xt[0], Xl, Xtl, L.x_stride, mp, np, m, n, normpart, L.tiles);
     if (hipError_t e = last_launch(); e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(norm_kernel, dim3(count), dim3(256), 0, st, normpart, L.tiles, scal);
@@ -976,26 +1079,19 @@ static hipError_t run_large_t(const LargeArgs& g, hipStream_t st) {
   const int steps = g.sc.ns_steps;
   if (steps == 0) {
     hipLaunchKernelGGL((ns0_kernel<PT, XT>), dim3(unsigned(std::min<int64_t>(4096, (m * n + 255) / 256)), count),
-                       dim3(256), 0, st, g.tab, g.sc, X, mp, np, m, n, scal);
+                       dim3(256), 0, st, g.tab, g.sc, X, Xl, mp, np, m, n, scal);
     return last_launch();
   }
   int cur = 0;
   for (int k = 0; k < steps; ++k) {
     const int last = (k == steps - 1);
     if constexpr (sizeof(XT) == 2) {
-      const int G = g.grouped ? group_len(k, steps) : 1;
-      if (G >= 2) {
-        const int lastG = (k + G == steps);
-        const hipError_t e = (g.tile == 256) ? ns_group_bf16<256, PT>(g, st, k, G, cur, lastG)
-                                             : ns_group_bf16<128, PT>(g, st, k, G, cur, lastG);
-        if (e != hipSuccess) return e;
-        k += G - 1;  // the group took steps k .. k + G - 1
-        cur ^= 1;
-        continue;
-      }
-      const hipError_t e = (g.tile == 256) ? ns_step_bf16<256, PT>(g, st, k, cur, last)
-                                           : ns_step_bf16<128, PT>(g, st, k, cur, last);
+      const int G = group_len(k, steps, g.whole);
+      const int lastG = (k + G == steps);
+      const hipError_t e = (g.tile == 256) ? ns_group_bf16<256, PT>(g, st, k, G, cur, lastG)
+                                           : ns_group_bf16<128, PT>(g, st, k, G, cur, lastG);
       if (e != hipSuccess) return e;
+      k += G - 1;  // the group took steps k .. k + G - 1
     } else {
       float* Pf = (float*)(ws + L.poff);
       const int Tm = int(mp / GF_M), Tn = int(np / GF_M);

@@ -39,12 +39,63 @@ namespace muon {
 namespace {
 
 constexpr int kNB = 8;            // 32-column blocks per wave (slab <= 4 * 8 * 32 = 1024 columns)
-constexpr int kLdr = 36;          // LDS column stride (bf16) of the transpose staging
+constexpr int kLdr = 36;          // LDS column stride (bf16) of the Gram's restaging
+constexpr int kLdf = 36;          // LDS column stride (fp32) of the momentum block's staging
 constexpr int kPartW = 544;       // 8-byte words per published slab partial (upper triangle <= 528, + sum of squares)
 constexpr int kCoherent = 16;     // buffer cache policy: device-coherent access (sc1)
 constexpr int kGather = 12;       // partial words each thread has in flight while gathering
 
 __device__ __forceinline__ int row_of(int r, int h) { return ((r >> 2) << 3) + (h << 2) + (r & 3); }
+
+// In muon_step the NS input U (fp32) is held as hi = bf16(U) in registers
+// and its remainder lo = U - hi (exact in fp32) as an 8-bit code against
+// hi's exponent E: code = round(lo * 2^(15 - E)), lo ~ code * 2^(E - 15).
+// |lo| is at most half an ulp of hi, 2^(E - 8), so |code| <= 128 (clamped
+// to 127) and the code carries 8 more bits of U: hi + lo holds U to about
+// 2^-16 relative.  The decoded lo is exactly a bf16 value.  Hi below 2^-111
+// (or not finite) gets code 0.
+__device__ __forceinline__ uint32_t lo_code(float u, uint32_t hi) {
+  const uint32_t ef = (hi >> 7) & 0xffu;
+  const bool ok = ef - 16u <= 238u;                                         // 16 <= ef <= 254
+  const float lo = u - __uint_as_float(hi << 16);
+  const float scale = __uint_as_float((269u << 23) - ((hi << 16) & 0x7f800000u));  // 2^(15 - E)
+  const float c = __builtin_amdgcn_fmed3f(rintf(lo * scale), -127.f, 127.f);
+  return ok ? (uint32_t(int(c)) & 0xffu) : 0u;
+}
+// lo (as bf16 bits) of the value whose hi is `hi` and whose code is the
+// byte `code` (bits 0-7): code * 2^(E - 15), the code carrying lo's sign;
+// 0 for hi below 2^-111
+__device__ __forceinline__ uint32_t lo_decode(uint32_t hi, uint32_t code) {
+  const uint32_t ex = (hi << 16) & 0x7f800000u;        // exponent of hi, fp32 position
+  const bool ok = (ex >> 23) > 15u;
+  const float scale = __uint_as_float(ex - (15u << 23));  // 2^(E - 15)
+  // the byte as a signed value by a shift pair (the form sbfe + conversion
+  // was lowered to an unsigned conversion of the sign-extended byte)
+  const float v = float(int(code << 24) >> 24) * scale;
+  return ok ? uint32_t(f2bf(v)) : 0u;
+}
+// codes of the 16 values of a lane's block (U in u, hi in the bf16 pairs
+// x), value r in byte r % 4 of word r / 4
+__device__ __forceinline__ void lo_codes(const float* u, const uint32_t* x, uint32_t* code) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t c = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int r = 4 * w + b;
+      c |= lo_code(u[r], (x[r >> 1] >> (16 * (r & 1))) & 0xffffu) << (8 * b);
+    }
+    code[w] = c;
+  }
+}
+// lo as bf16 pairs in the register layout of x (hi pairs)
+__device__ __forceinline__ void lo_words(const uint32_t* x, const uint32_t* code, uint32_t* xl) {
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    const uint32_t c = code[d >> 1] >> (16 * (d & 1));
+    xl[d] = lo_decode(x[d] & 0xffffu, c & 0xffu) | (lo_decode(x[d] >> 16, (c >> 8) & 0xffu) << 16);
+  }
+}
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
 // (lgkmcnt 0) but not for its global memory accesses, so the momentum stores
@@ -93,14 +144,25 @@ __device__ __forceinline__ void tri_ij(int e, int m, int& i, int& j) {
 // below the byte offset that masks a lane
 static_assert(uint64_t(kSkinnyCapacity) * 2 * kPartW * 8 < kOobByte, "partial buffer reaches the lane mask");
 
+// LDS of one workgroup.  The momentum phase stages blocks through `stage`;
+// the Gram-space recurrence keeps Q and its successor (fp32) there, and the
+// apply finds the Q operand table (`pop`) there.  `red` (wave partials,
+// gathered slab partials, a copy of Q, the O staging of the apply) shares
+// its bytes with the Gram-space matrices, which live between the gather and
+// the end of the recurrence.  For m <= 24 (KS = 6) the lo codes of U stay
+// in LDS from the momentum phase to the apply: 12 bytes per lane, block and
+// wave (24 KB), which keeps 3 workgroups per CU.
+template <int KS>
 struct SkShared {
-  uint16_t stage[4][32 * kLdr];   // per-wave transpose staging, column-major [col][row]
-  // per-wave Gram partials; gathered slab partials; the m x m matrices of the
-  // Gram-space recurrence; per-wave O staging at the end
-  float red[4][32 * 33];
-  float A[32][33];
-  float mat[2][32][33];
-  u16x8 pop[2][2][64];            // Q operand registers per lane: [k-step][hi, lo][lane]
+  alignas(16) uint16_t stage[4][32 * kLdr];
+  union {
+    float red[4][32 * 33];
+    struct {
+      float A[32][33];
+      float mat[2][32][33];
+    } gs;
+  } u;
+  alignas(16) uint8_t codes[KS == 6 ? 4 * kNB * 64 * 12 : 16];
   float ss[4];
   int fail;                       // set when a wait of this workgroup timed out
 };
@@ -175,13 +237,15 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
                                                         int S, int64_t slab_w, float* __restrict__ part,
                                                         uint32_t* __restrict__ sync, unsigned spin_limit,
                                                         uint32_t epoch_host, const uint32_t* __restrict__ epoch_dev,
-                                                        uint32_t* __restrict__ host_flag) {
+                                                        uint32_t* __restrict__ host_flag, uint8_t* __restrict__ lobuf) {
   static_assert(sizeof(PT) == 2, "skinny path is bf16");
   // launches recorded into a graph read their number from the counter that
   // the one-thread kernel before them advanced; others get it from the host
   const uint32_t epoch = epoch_dev ? (kDeviceEpochBit | (*epoch_dev & (kDeviceEpochBit - 1))) : epoch_host;
   constexpr bool step_mode = MODE == 0;
-  __shared__ SkShared sh;
+  __shared__ SkShared<KS> sh;
+  // the Q operand registers of the apply, per lane: [k-step][hi, lo][lane]
+  u16x8 (*pop)[2][64] = reinterpret_cast<u16x8 (*)[2][64]>(&sh.stage[0][0]);
   if (threadIdx.x == 0) sh.fail = 0;  // read only after several barriers
   const int z = blockIdx.x / S, s = blockIdx.x % S;
   // copy this matrix's descriptor out of the argument block
@@ -204,6 +268,29 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   const uint32_t part_z = uint32_t(z) * 2u * uint32_t(S) * uint32_t(kPartW);  // word index
   const int v = threadIdx.x >> 6;  // wave index (uniform within the wave)
   const int ntri = m * (m + 1) / 2;  // published Gram entries
+  // lo codes of U (muon_step), in the register layout: kLoB bytes per lane,
+  // wave and block of each workgroup (12 when m <= 24: a lane's last 4 values
+  // are then padding rows)
+  constexpr uint32_t kLoB = (KS == 6) ? 12u : 16u;
+  const rsrc_t rL = make_rsrc(lobuf, step_mode ? uint32_t(gridDim.x) * 4u * kNB * 64u * 16u : 0u);
+  auto lo_off = [&](int q, int lane) -> uint32_t {
+    return ((uint32_t(blockIdx.x) * 4u + uint32_t(v)) * kNB + uint32_t(q)) * 64u * kLoB + uint32_t(lane) * kLoB;
+  };
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+  auto lo_store = [&](int q, int lane, const uint32_t* code) {
+    if constexpr (kLoB == 12u)
+      __builtin_amdgcn_raw_buffer_store_b96(u32x3{code[0], code[1], code[2]}, rL, int(lo_off(q, lane)), 0, 0);
+    else
+      buf_st_b128(rL, lo_off(q, lane), u32x4{code[0], code[1], code[2], code[3]});
+  };
+  auto lo_load = [&](int q, int lane) -> u32x4 {
+    if constexpr (kLoB == 12u) {
+      const u32x3 c = __builtin_amdgcn_raw_buffer_load_b96(rL, int(lo_off(q, lane)), 0, 0);
+      return u32x4{c[0], c[1], c[2], 0u};
+    } else {
+      return buf_ld_b128(rL, lo_off(q, lane));
+    }
+  };
 
   // Thread-index-derived values are re-derived through opaque() at the top of
   // each phase: otherwise the compiler hoists every address it can out of
@@ -239,6 +326,8 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   // wave's LDS area, read it back row-per-lane, one MFMA per 16 columns.
   // Taken per block inside the momentum loop, while the next block's loads
   // are in flight.
+  // With the lo part xl (muon_step), X0 X0^T ~ Xh Xh^T + Xh Xl^T + Xl Xh^T,
+  // taken in that order per 16 columns.
   auto gram_block = [&](const uint32_t* x, f32x16& gacc, int lane) {
     const int h = lane >> 5, cl = lane & 31;
 #pragma unroll
@@ -303,6 +392,29 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
 #pragma unroll
       for (int d = 0; d < 8; ++d) xw[q][d] = *(const uint32_t*)(stg + cl * kLdr + row_of(2 * d, h));
       __builtin_amdgcn_wave_barrier();
+      if (step_mode) {
+        // each code goes straight to its place in the register layout:
+        // row r is value 4 (r / 8) + r % 4 of lane 32 ((r / 4) % 2) + column
+        const int dl = ((r >> 2) & 1) * 32 + 16 * hc, dv = 4 * (r >> 3) + (r & 3);
+        if constexpr (KS == 6) {
+          uint8_t* cb = sh.codes + (v * kNB + q) * 64 * 12;
+          if (r < m) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) cb[(dl + j) * 12 + dv] = uint8_t(lo_code(u[j], f2bf(u[j])));
+          }
+        } else {
+          // through this wave's staging area (free until the Gram restages
+          // the block), then one 16-byte store per lane
+          uint8_t* st8 = reinterpret_cast<uint8_t*>(stg);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) st8[(dl + j) * 16 + dv] = uint8_t(lo_code(u[j], f2bf(u[j])));
+          __builtin_amdgcn_wave_barrier();
+          const u32x4 cw = *(const u32x4*)(st8 + lane * 16);
+          __builtin_amdgcn_wave_barrier();
+          const uint32_t code[4] = {cw[0], cw[1], cw[2], cw[3]};
+          lo_store(q, lane, code);
+        }
+      }
     } else {
       const int col = c0 + (v * kNB + q) * 32 + cl;
       // all loads of the block first (stores to M below could alias later
@@ -328,6 +440,16 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       }
 #pragma unroll
       for (int d = 0; d < 8; ++d) xw[q][d] = f2bf2(uu[2 * d], uu[2 * d + 1]);
+      if (step_mode) {
+        uint32_t code[4];
+        lo_codes(uu, xw[q], code);
+        if constexpr (KS == 6) {
+          uint32_t* cw = reinterpret_cast<uint32_t*>(sh.codes + ((v * kNB + q) * 64 + lane) * 12);
+          cw[0] = code[0]; cw[1] = code[1]; cw[2] = code[2];
+        } else {
+          lo_store(q, lane, code);
+        }
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     gram_block(xw[q], gacc, opaque(int(threadIdx.x)) & 63);
@@ -339,7 +461,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   auto publish = [&](const f32x16& gacc, int k, bool with_ss) {
     const int t = opaque(int(threadIdx.x)), lane = t & 63, h = lane >> 5, cl = lane & 31;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sh.red[v][row_of(r, h) * 32 + cl] = gacc[r];
+    for (int r = 0; r < 16; ++r) sh.u.red[v][row_of(r, h) * 32 + cl] = gacc[r];
     float tot = 0.f;
     if (with_ss) tot = sum_256(ss, sh.ss);  // contains a barrier
     lds_barrier();
@@ -349,7 +471,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       int i, j;
       tri_ij(e, m, i, j);
       const int o = i * 32 + j;
-      const float val = (sh.red[0][o] + sh.red[1][o]) + (sh.red[2][o] + sh.red[3][o]);
+      const float val = (sh.u.red[0][o] + sh.u.red[1][o]) + (sh.u.red[2][o] + sh.u.red[3][o]);
       const uint64_t w = tagged(val, tag);
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), rP, int((dst + e) * 8), 0, kCoherent);
     }
@@ -360,19 +482,19 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   };
 
   // Gather the slab partials once their tags show up and combine them in
-  // slab order (identical in every workgroup): sh.A = s^2 * X0 X0^T (padded
+  // slab order (identical in every workgroup): A = s^2 * X0 X0^T (padded
   // with zeros to 32 x 32) and s_out = s.
   auto gather_a = [&](int k, bool first, float& s_out) {
     const int t = opaque(int(threadIdx.x));
     const uint32_t tag = (epoch << 5) | uint32_t(k + 1);
     const uint32_t src = part_z + uint32_t(k & 1) * S * kPartW;
-    lds_barrier();  // every thread has read sh.red for its publish before gbuf (= sh.red) is written
+    lds_barrier();  // every thread has read red for its publish before gbuf (= red) is written
     // words per slab: the triangle, plus the sum of squares on the first step
     const int nw = ntri + (first ? 1 : 0);
     // The per-wave staging area (free between publish and the last apply)
     // holds `per` slabs of words at a time.  Each thread has up to kGather
     // loads in flight, then waits for their tags and parks the values in LDS.
-    float* gbuf = &sh.red[0][0];
+    float* gbuf = &sh.u.red[0][0];
     const int per = min(S, min(4 * 32 * 33, 256 * kGather) / nw);
     float acc[3] = {0.f, 0.f, 0.f};  // this thread's entries t, t+256, t+512
     for (int q0 = 0; q0 < S; q0 += per) {
@@ -428,7 +550,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       s_out = sn;
     }
     // zero the padded A, then fill both triangles
-    for (int e = t; e < 32 * 33; e += 256) (&sh.A[0][0])[e] = 0.f;
+    for (int e = t; e < 32 * 33; e += 256) (&sh.u.gs.A[0][0])[e] = 0.f;
     lds_barrier();
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
@@ -436,20 +558,20 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       if (e < ntri) {
         int i, j;
         tri_ij(e, m, i, j);
-        sh.A[i][j] = acc[r] * s2;
-        sh.A[j][i] = acc[r] * s2;
+        sh.u.gs.A[i][j] = acc[r] * s2;
+        sh.u.gs.A[j][i] = acc[r] * s2;
       }
     }
     lds_barrier();
   };
 
-  // Gram-space NS: from sh.A = A0 and s, run the recurrence and leave Q_K
-  // (hi/lo bf16) in the per-lane MFMA operand layout sh.pop.
+  // Gram-space NS: from A = A0 and s, run the recurrence and leave Q_K
+  // (hi/lo bf16) in the per-lane MFMA operand layout `pop`.
   auto gram_space_ns = [&](float snorm) {
     const int t = opaque(int(threadIdx.x));
-    float (*A)[33] = sh.A;
-    float (*P)[33] = sh.mat[0];
-    float (*T)[33] = sh.mat[1];
+    float (*A)[33] = sh.u.gs.A;
+    float (*P)[33] = sh.u.gs.mat[0];
+    float (*T)[33] = sh.u.gs.mat[1];
     // Q and its successor live in the (now idle) transpose staging area
     float (*Q)[33] = (float (*)[33])(void*)&sh.stage[0][0];
     float (*Qn)[33] = Q + 32;
@@ -477,27 +599,38 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       }
       { float (*tq)[33] = Q; Q = Qn; Qn = tq; }
     }
+    // Q lives in the staging area, where its operand table goes: copy it to
+    // `red` (free again: the Gram-space matrices are dead) first
+    float (*Qc)[33] = reinterpret_cast<float (*)[33]>(&sh.u.red[0][0]);
+    for (int e = t; e < 32 * 32; e += 256) Qc[e >> 5][e & 31] = Q[e >> 5][e & 31];
+    lds_barrier();
     // Q (fp32) -> hi/lo bf16 operand registers: Q[i][kr] is k-slot q of lane
     // (h, i) in k-step tt, where X0 row kr sits at k-slot q of lane half h
     for (int e = t; e < 32 * 32; e += 256) {
       const int i = e >> 5, kr = e & 31;
-      const float qv = Q[i][kr];
+      const float qv = Qc[i][kr];
       const uint16_t hi = f2bf(qv);
       const int tt = kr >> 4, hh = (kr >> 2) & 1, q = ((kr >> 3) & 1) * 4 + (kr & 3);
-      sh.pop[tt][0][hh * 32 + i][q] = hi;
-      sh.pop[tt][1][hh * 32 + i][q] = f2bf(qv - bf2f(hi));
+      pop[tt][0][hh * 32 + i][q] = hi;
+      pop[tt][1][hh * 32 + i][q] = f2bf(qv - bf2f(hi));
     }
     lds_barrier();
   };
 
-  auto apply = [&](const uint32_t* x, int lane) {
+  // O = (Qh + Ql) X0 for one block, with X0 = Xh + Xl in muon_step: per 16
+  // rows Qh Xh, Ql Xh, then Qh Xl
+  auto apply = [&](const uint32_t* x, const uint32_t* xl, int lane) {
     const bf16x8 x0 = __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], x[2], x[3]});
     const bf16x8 x1 = __builtin_bit_cast(bf16x8, u32x4{x[4], x[5], x[6], x[7]});
     f32x16 acc = f32x16{};
-    acc = mfma32x32x16(as_bf16x8(sh.pop[0][0][lane]), x0, acc);
-    acc = mfma32x32x16(as_bf16x8(sh.pop[0][1][lane]), x0, acc);
-    acc = mfma32x32x16(as_bf16x8(sh.pop[1][0][lane]), x1, acc);
-    acc = mfma32x32x16(as_bf16x8(sh.pop[1][1][lane]), x1, acc);
+    acc = mfma32x32x16(as_bf16x8(pop[0][0][lane]), x0, acc);
+    acc = mfma32x32x16(as_bf16x8(pop[0][1][lane]), x0, acc);
+    if (step_mode)
+      acc = mfma32x32x16(as_bf16x8(pop[0][0][lane]), __builtin_bit_cast(bf16x8, u32x4{xl[0], xl[1], xl[2], xl[3]}), acc);
+    acc = mfma32x32x16(as_bf16x8(pop[1][0][lane]), x1, acc);
+    acc = mfma32x32x16(as_bf16x8(pop[1][1][lane]), x1, acc);
+    if (step_mode)
+      acc = mfma32x32x16(as_bf16x8(pop[1][0][lane]), __builtin_bit_cast(bf16x8, u32x4{xl[4], xl[5], xl[6], xl[7]}), acc);
     return acc;
   };
 
@@ -508,7 +641,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
     const int lane = opaque(int(threadIdx.x)) & 63, h = lane >> 5, cl = lane & 31;
     if (full(q)) {
       // O through LDS (fp32, column-major, stride 33) to row-major vectors
-      float* fst = sh.red[v];
+      float* fst = sh.u.red[v];
 #pragma unroll
       for (int r = 0; r < 16; ++r) fst[cl * 33 + row_of(r, h)] = o[r];
       __builtin_amdgcn_wave_barrier();
@@ -564,9 +697,28 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   {
     const int lane = opaque(int(threadIdx.x)) & 63;
     const bool failed = sh.fail != 0;
+    // every block's lo codes are requested at once, so that their latency is
+    // paid once
+    // (m > 24: from the workspace; m <= 24: kept in LDS)
+    u32x4 cw[KS == 6 ? 1 : kNB];
+    if constexpr (step_mode && KS != 6) {
+#pragma unroll
+      for (int q = 0; q < kNB; ++q) cw[q] = lo_load(q, lane);
+    }
 #pragma unroll
     for (int q = 0; q < kNB; ++q) {
-      const f32x16 acc = apply(xw[q], lane);
+      uint32_t xl[8];
+      if (step_mode) {
+        uint32_t code[4];
+        if constexpr (KS == 6) {
+          const uint32_t* cp = reinterpret_cast<const uint32_t*>(sh.codes + ((v * kNB + q) * 64 + lane) * 12);
+          code[0] = cp[0]; code[1] = cp[1]; code[2] = cp[2]; code[3] = 0u;
+        } else {
+          code[0] = cw[q][0]; code[1] = cw[q][1]; code[2] = cw[q][2]; code[3] = cw[q][3];
+        }
+        lo_words(xw[q], code, xl);
+      }
+      const f32x16 acc = apply(xw[q], xl, lane);
       emit_block(acc, q, failed);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -577,7 +729,7 @@ template <int MODE, int KS>
 static void launch_skinny(const SkinnyArgs& g, hipStream_t st) {
   const unsigned grid = unsigned(g.count * g.slabs);
   hipLaunchKernelGGL((skinny_kernel<uint16_t, MODE, KS>), dim3(grid), dim3(256), 0, st, g.tab, g.sc, g.m, g.n,
-                     g.slabs, g.slab_w, g.part, g.sync, g.spin_limit, g.epoch, g.epoch_dev, g.host_flag);
+                     g.slabs, g.slab_w, g.part, g.sync, g.spin_limit, g.epoch, g.epoch_dev, g.host_flag, g.lobuf);
 }
 
 hipError_t run_skinny(const SkinnyArgs& g, hipStream_t st) {

@@ -19,7 +19,9 @@ struct LargeArgs {
   int tile;          // bf16 GEMM tile (128 or 256)
   int cus;           // compute units of the device (one 256-tile workgroup each)
   bool bf16;
-  bool grouped;      // NS steps taken in groups (bf16 path)
+  bool whole;        // bf16 path: all NS steps in one group
+  bool precise;      // bf16 path: split m x m chain with lo planes
+  bool x0_lo;        // bf16 muon_step: X_0 carries its lo plane
 };
 
 // u32 indices, in the workspace's sync region, of the skinny path's timeout
@@ -45,9 +47,22 @@ struct SkinnyArgs {
   uint32_t epoch;    // distinct per launch: tags the published partials
   const uint32_t* epoch_dev;  // if set, the epoch is read from here (graph capture)
   uint32_t* host_flag;        // host-visible word set on a timed-out wait, or null
+  uint8_t* lobuf;             // muon_step: lo codes of U, 16 bytes per lane and block
 };
 
 hipError_t run_large(const LargeArgs& a, hipStream_t st);
+
+// Optional timing of the MFMA path's apply launches (the dominant kernel of
+// large workloads) with HIP events on the launch stream, for benchmarks.
+// While enabled, every apply (its main launch and a partial-round launch, if
+// any) is bracketed by an event pair, up to kTimerPairs pairs.
+constexpr int kTimerPairs = 4096;
+void timer_begin(hipStream_t st);
+void timer_end(hipStream_t st, double alg_flops, double exec_flops);
+// enable (creating the events on first use) or disable; read drains and
+// resets the totals: host waits for the recorded events
+hipError_t timer_enable(bool on);
+hipError_t timer_read(double* ms, int64_t* launches, double* alg_flops, double* exec_flops);
 hipError_t run_skinny(const SkinnyArgs& a, hipStream_t st);
 int skinny_max_blocks_per_cu();
 // one-thread kernel: counter <- counter + 1 (numbers the next skinny launch)

@@ -56,7 +56,9 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
     L.poff = take(size_t(count) * size_t(mp) * size_t(mp) * 4);  // full fp32 P
   }
   L.pdiag = take(size_t(count) * size_t(mp) * 4);
-  if (g.grouped) {
+  if (param_dt == MUON_BF16) {
+    L.xl = take(xb);
+    L.xtl = take(xb);
     L.th = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
     L.poff2 = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
     L.pdiag2 = take(size_t(count) * size_t(mp) * 4);
@@ -64,6 +66,13 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
     L.roff1 = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
     L.rdiag0 = take(size_t(count) * size_t(mp) * 4);
     L.rdiag1 = take(size_t(count) * size_t(mp) * 4);
+    {  // the precise chain's lo planes (also taken by the lean recipe beyond kLeanMaxSteps steps)
+      L.tl = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+      L.poffl0 = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+      L.poffl1 = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+      L.roffl0 = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+      L.roffl1 = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
+    }
   }
   L.normpart = take(size_t(count) * size_t(L.tiles) * 4);
   L.scal = take(size_t(count) * 4 * 4);
@@ -71,13 +80,9 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
   return L;
 }
 
-bool mfma_grouped(int64_t m, int64_t n) {
-  // Only where grouped steps have been shown to keep O as accurate as single
-  // steps (m >= 512, wide shapes), and where the saving outweighs the extra
-  // launches and the m x m epilogue traffic: at n = 1.33 m (8 x [1536, 2048])
-  // grouped steps measured 20% slower than single steps (pairs 15%), at
-  // n = 3.5 m ([8192, 28672], [4096, 14336]) 35-40% faster.
-  return m >= 512 && n >= 2 * m;
+NsRecipe ns_recipe(int64_t m, int64_t n) {
+  (void)n;
+  return NsRecipe{m < kWholeBelowM, m < kLeanFromM};
 }
 
 double ns_cost(int64_t rows, int64_t cols) {
@@ -121,8 +126,15 @@ int32_t mfma_tile(int64_t m, int64_t n, int64_t count) {
   return (sym >= 256 && full >= 512 && big <= 1.10 * small) ? int32_t(kMfmaTileBig) : int32_t(kMfmaTile);
 }
 
+size_t skinny_lo_offset(const Group& g, int32_t count) {
+  return align256(size_t(count) * 2 * size_t(g.slabs) * size_t(kSkinnyPartStride) * 4);
+}
+
 size_t skinny_bytes(const Group& g, int32_t count) {
-  return size_t(count) * 2 * size_t(g.slabs) * size_t(kSkinnyPartStride) * 4;
+  // slab partials, then (m > 24; smaller m keeps them in LDS) the lo codes
+  // of U: 16 bytes per lane, block and wave
+  return skinny_lo_offset(g, count) +
+         (g.m > 24 ? size_t(count) * size_t(g.slabs) * size_t(kSkinnyWaves * kSkinnyBlocksPerWave * 64 * 16) : 0);
 }
 
 muon_status build_plan(const muon_shape* shapes, int32_t n_params, muon_dtype param_dt,
@@ -194,7 +206,11 @@ muon_status build_plan(const muon_shape* shapes, int32_t n_params, muon_dtype pa
       g.chunks = split_even(count, cap);
     } else {
       g.tile = (g.path == PATH_MFMA) ? mfma_tile(g.m, g.n, count) : int32_t(kF32Tile);
-      g.grouped = (g.path == PATH_MFMA) && mfma_grouped(g.m, g.n);
+      if (g.path == PATH_MFMA) {
+        const NsRecipe r = ns_recipe(g.m, g.n);
+        g.whole = r.whole;
+        g.precise = r.precise;
+      }
       const int64_t t = g.tile;
       g.mp = round_up(g.m, t);
       g.np = round_up(g.n, t);

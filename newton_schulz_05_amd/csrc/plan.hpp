@@ -55,7 +55,9 @@ struct Chunk {
 // MFMA and fp32 paths.  Per-matrix strides are in elements of the buffer type.
 struct LargeLayout {
   size_t x, xt0, xt1, a, h, l, poff, pdiag, normpart, scal;
-  size_t th, poff2, pdiag2, roff0, roff1, rdiag0, rdiag1;  // grouped steps only, else 0
+  size_t th, poff2, pdiag2, roff0, roff1, rdiag0, rdiag1;  // bf16 path (grouped steps), else 0
+  size_t xl, xtl;                                          // bf16 path: lo planes of X_0 and its transpose
+  size_t tl, poffl0, poffl1, roffl0, roffl1;               // bf16 path: lo planes of T, P, R (precise chain)
   int64_t x_stride, a_stride, tiles;  // elements per matrix (X / A) and momentum tiles per matrix
   size_t bytes;                       // total bytes of the chunk region
 };
@@ -68,7 +70,8 @@ struct Group {
   std::vector<Chunk> chunks;
   int64_t mp = 0, np = 0;      // padded dims (MFMA / fp32 paths)
   int32_t tile = 0;            // MFMA path: GEMM output tile (128 or 256)
-  bool grouped = false;        // MFMA path: NS steps taken in groups (mfma_grouped)
+  bool whole = false;          // MFMA path: all NS steps in one group (ns_recipe)
+  bool precise = false;        // MFMA path: split m x m chain and lo planes (ns_recipe)
   int32_t slabs = 0;           // skinny: column slabs per matrix
   int64_t slab_w = 0;          // skinny: columns per slab (multiple of 32)
   int32_t max_chunk = 0;       // largest chunk of this group
@@ -91,8 +94,10 @@ muon_status build_plan(const muon_shape* shapes, int32_t n_params, muon_dtype pa
 // Layout of one chunk of `count` matrices of group g (MFMA / fp32 paths).
 LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt);
 
-// Bytes of the skinny partial-sum buffer for one chunk.
+// Bytes of the skinny path's region for one chunk: the slab partials, then
+// (from skinny_lo_offset) the lo codes of U.
 size_t skinny_bytes(const Group& g, int32_t count);
+size_t skinny_lo_offset(const Group& g, int32_t count);
 
 // NS cost 3 m^2 n + m^3 of one matrix (m = min, n = max of its dimensions).
 double ns_cost(int64_t rows, int64_t cols);
@@ -106,13 +111,35 @@ void assign_greedy(const Plan& P, int32_t n_ranks, std::vector<int32_t>* owner, 
 // GEMM tile of an MFMA-path group of `count` matrices of wide shape [m, n].
 int32_t mfma_tile(int64_t m, int64_t n, int64_t count);
 
-// Whether an MFMA-path group of wide shape [m, n] takes its NS steps in
-// groups: steps k .. k+G-1 with one Gram of X_k and one apply of
+// How an MFMA-path group of wide shape [m, n] takes its NS steps.  Every
+// group of steps k .. k+G-1 has one Gram of X_k and one apply of
 // R = P_{k+G-1} ... P_k, the A_j in between formed in the m x m space
-// (A_{j+1} = P_j A_j P_j).  A group of G steps costs 3 m^2 n + (4 G - 3) m^3
-// flops (single-product A^2) instead of G (3 m^2 n + m^3), a saving once
-// n > m; taken for m >= 512 and n >= 2 m.
-bool mfma_grouped(int64_t m, int64_t n);
+// (A_{j+1} = P_j A_j P_j); a group of G steps costs 3 m^2 n + (4 G - 3) m^3
+// flops with single products.
+//   whole   : all steps in one group (m < kWholeBelowM), else the first
+//             min(4, N - 1) steps, then pairs, then a single step;
+//   precise : the m x m chain takes split-bf16 products with lo planes of
+//             P, T and R, the first Gram uses X_0's lo plane and the applies
+//             R's (m < kLeanFromM).  The lean recipe (m >= kLeanFromM) keeps
+//             the chain in single products and only the first apply uses
+//             X_0's lo plane.
+// The thresholds come from an emulation of these roundings on inputs with
+// singular values spread over [1e-2, 1] and [1e-3, 1] and rank-m/8 inputs:
+// the lean recipe keeps the relative Frobenius error of O under 1e-2 at
+// m = 4096 (at most 7.5e-3) but not at m = 1536 (1.5e-2 on rank-m/8), and
+// below m = 512 grouping with a bf16 chain loses accuracy (4.5e-2 at
+// 64 x 200) where one whole group with the split chain stays under 2e-3.
+// The lean recipe also holds only up to kLeanMaxSteps NS steps (at 8 steps
+// [4096, 4096] reached 1.4e-2 on the GPU, the precise recipe 3.5e-3 at
+// [1024, 1024]); a call with more steps takes the precise chain, whose lo
+// planes every bf16 workspace therefore holds.
+constexpr int64_t kWholeBelowM = 512;
+constexpr int64_t kLeanFromM = 4096;
+constexpr int kLeanMaxSteps = 5;
+struct NsRecipe {
+  bool whole, precise;
+};
+NsRecipe ns_recipe(int64_t m, int64_t n);
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }

@@ -111,3 +111,35 @@ def numpy_normal(shape, seed: int, std: float, dtype: torch.dtype) -> torch.Tens
     if std != 1.0:
         x *= np.float32(std)
     return torch.from_numpy(x).to(dtype)
+
+
+def spectral(rows: int, cols: int, kind: str, seed: int, peak: float = 0.05,
+             dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """A seeded [rows, cols] matrix with a prescribed singular-value
+    spectrum, drawn on the host with NumPy's PCG64 generator and rounded to
+    `dtype`, scaled so that its largest entry is `peak`.  With m = min and
+    n = max of the dimensions:
+      'logD'  : Q1 diag(s) Q2^T with s_i = 10^(-D i / (m - 1)), i = 0 .. m-1
+                (singular values log-spaced over [10^-D, 1]), Q1 [m, m] and
+                Q2 [n, m] orthonormal from QR of Gaussian matrices;
+      'rankK' : the product of Gaussian [m, r] and [r, n] matrices with
+                r = max(1, m // K) (rank m / K before the rounding to dtype).
+    Stands in for a momentum whose spectrum spreads over decades."""
+    import numpy as np
+
+    m, n = min(rows, cols), max(rows, cols)
+    rng = np.random.Generator(np.random.PCG64(int(seed)))
+    if kind.startswith("log"):
+        d = float(kind[3:])
+        q1, _ = np.linalg.qr(rng.standard_normal((m, m)))
+        q2, _ = np.linalg.qr(rng.standard_normal((n, m)))
+        z = (q1 * np.logspace(-d, 0.0, m)) @ q2.T
+    elif kind.startswith("rank"):
+        r = max(1, m // int(kind[4:]))
+        z = rng.standard_normal((m, r)) @ rng.standard_normal((r, n))
+    else:
+        raise ValueError(f"unknown spectrum kind {kind!r}")
+    z *= peak / np.max(np.abs(z))
+    if rows > cols:
+        z = z.T
+    return torch.from_numpy(np.ascontiguousarray(z, dtype=np.float32)).to(dtype)

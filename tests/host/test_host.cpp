@@ -69,6 +69,12 @@ static void check_plan(const Plan& P) {
       CHECK(L.tiles == ceil_div(g.m, kMomTile) * ceil_div(g.n, kMomTile));
       const size_t offs[] = {L.x, L.xt0, L.xt1, L.a, L.poff, L.pdiag, L.normpart, L.scal};
       for (size_t o : offs) CHECK(o % 256 == 0 && o < L.bytes);
+      if (P.param_dt == MUON_BF16) {
+        const size_t lo[] = {L.xl, L.xtl, L.th, L.poff2, L.roff0, L.roff1, L.rdiag0, L.rdiag1};
+        for (size_t o : lo) CHECK(o != 0 && o % 256 == 0 && o < L.bytes);
+        const size_t pl[] = {L.tl, L.poffl0, L.poffl1, L.roffl0, L.roffl1};
+        for (size_t o : pl) CHECK(o != 0 && o % 256 == 0 && o < L.bytes);
+      }
       CHECK(L.xt0 >= L.x + size_t(g.max_chunk) * size_t(L.x_stride) * (P.param_dt == MUON_BF16 ? 2 : 4));
       CHECK(L.scal + size_t(g.max_chunk) * 16 <= L.bytes);
       need = std::max(need, L.bytes);
@@ -98,10 +104,13 @@ static void test_workload_plans() {
   Plan p4 = make(c4);
   check_plan(p4);
   CHECK(p4.groups.size() == 2 && p4.groups[1].mats.size() == 96 && p4.groups[1].n_tr == 64);
-  CHECK(p4.groups[0].tile == 256 && p4.groups[1].grouped && !p4.groups[0].grouped);
+  CHECK(p4.groups[0].tile == 256 && !p4.groups[0].whole && !p4.groups[0].precise && !p4.groups[1].precise);
+  CHECK(p3.groups[0].precise && !p3.groups[0].whole);
   Plan p5 = make({{1, 8192, 28672}, {1, 8192, 28672}});
   check_plan(p5);
-  CHECK(p5.groups[0].tile == 256 && p5.groups[0].grouped);
+  CHECK(p5.groups[0].tile == 256 && !p5.groups[0].precise);
+  Plan ps = make({{1, 100, 300}});
+  CHECK(ps.groups[0].whole && ps.groups[0].precise);
 }
 
 static void test_edge_plans() {

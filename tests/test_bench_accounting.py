@@ -25,33 +25,36 @@ def test_algorithmic_count_is_3m2n_plus_m3_per_step():
 
 
 def test_executed_count_grouped_steps_on_the_large_pair():
-    # 5 steps as a group of 4 and a single step.  Group: Gram m^2 n, A^2 in
-    # steps 0-2 as one product and in step 3 as three, T, A' and R for steps
-    # 1-3, apply 2 m^2 n.  Last step: Gram, split A^2, apply.
+    # lean recipe (m >= 4096), 5 steps as a group of 4 and a single step.
+    # Group: Gram m^2 n, A^2 in steps 0-2 as one product and in step 3 as
+    # three, T, A' and R for steps 1-3, apply with X_0's lo plane 2 x 2 m^2 n.
+    # Last step: Gram, split A^2, apply.
     m, n = 8192, 28672
-    group = 3 * m * m * n + (1 + 1 + 1 + 3) * m ** 3 + 3 * 3 * m ** 3
+    group = m * m * n + (1 + 1 + 1 + 3) * m ** 3 + 3 * 3 * m ** 3 + 2 * 2 * m * m * n
     single = 3 * m * m * n + 3 * m ** 3
     assert bench.executed_flops(WL.WORKLOADS["c5"]) == 2 * (group + single)
-    assert abs(bench.executed_flops(WL.WORKLOADS["c5"]) / 1e12 - 42.881) < 1e-3
 
 
 @pytest.mark.parametrize("ns_steps,groups", [(1, [1]), (2, [2]), (3, [2, 1]), (4, [3, 1]),
                                              (6, [4, 2]), (7, [4, 2, 1])])
 def test_executed_count_group_lengths(ns_steps, groups):
-    m, n = 600, 1300  # grouped: m >= 512, n >= 2 m
+    # precise recipe (512 <= m < 4096): first Gram with X_0's lo plane (3
+    # products), chain products split (3 each), applies with R's lo plane and,
+    # in the first group, X_0's
+    m, n = 600, 1300
     split = [k >= min(3, ns_steps - 2) for k in range(ns_steps)]
     want, k = 0, 0
     for g in groups:
-        want += 3 * m * m * n + sum((3 if split[k + j] else 1) * m ** 3 for j in range(g)) + 3 * (g - 1) * m ** 3
+        gram = (3 if k == 0 else 1) * m * m * n
+        apply = (3 if k == 0 else 2) * 2 * m * m * n
+        want += gram + sum((3 if split[k + j] else 1) * m ** 3 for j in range(g)) + 9 * (g - 1) * m ** 3 + apply
         k += g
     assert bench.executed_flops(_wl([(m, n)], ns_steps)) == want
 
 
-def test_executed_count_single_steps():
-    # square (not grouped, single-product A^2 in steps 0-2) and m < 512 (split
-    # in every step)
-    m = 512
-    want = 5 * 3 * m ** 3 + (1 + 1 + 1 + 3 + 3) * m ** 3
-    assert bench.executed_flops(_wl([(m, m)])) == want
+def test_executed_count_whole_group_below_512():
+    # m < 512: all 5 steps in one group, split A^2 everywhere, split chain,
+    # first Gram and the one apply with both lo planes
     m, n = 300, 700
-    assert bench.executed_flops(_wl([(n, m)])) == 5 * (3 * m * m * n + 3 * m ** 3)
+    want = 3 * m * m * n + 5 * 3 * m ** 3 + 9 * 4 * m ** 3 + 3 * 2 * m * m * n
+    assert bench.executed_flops(_wl([(n, m)])) == want

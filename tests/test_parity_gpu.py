@@ -124,22 +124,39 @@ def test_few_ns_steps(ns_steps, dt):
 
 @pytest.mark.parametrize("ns_steps", [1, 2, 3, 4, 5, 6, 7])
 def test_grouped_steps(ns_steps):
-    """Wide groups with m >= 512 and n >= 2 m take their NS steps in groups
-    (one Gram and one apply per group, the A in between formed in the m x m
-    space): the first min(4, steps - 1) steps, then pairs, then a single step
-    (1: one step; 2: a pair; 3: 2 + 1; 5: 4 + 1; 6: 4 + 2; 7: 4 + 2 + 1).  The
-    square member takes single steps (which also covers the single-product
-    A^2 of the first steps at every count).  Ragged padding (600 x 1300 pads
-    to 640 x 1408) and a tall member.  The square member sits out the 7-step
-    case: the bf16 recipe's own error on square shapes grows with the step
-    count and reaches ~9.5e-3 at 7 steps in a CPU emulation, with or without
-    the single-product A^2, too close to the 1e-2 bar (which is set for 5
-    steps)."""
-    shapes = [(512, 1024), (1300, 600)] + ([(512, 512)] if ns_steps <= 6 else [])
+    """MFMA-path groups with m >= 512 take their NS steps in groups (one Gram
+    and one apply per group, the A in between formed in the m x m space):
+    the first min(4, steps - 1) steps, then pairs, then a single step (1: one
+    step; 2: a pair; 3: 2 + 1; 5: 4 + 1; 6: 4 + 2; 7: 4 + 2 + 1), which also
+    covers the single-product A^2 of the first steps at every count.  Ragged
+    padding (600 x 1300 pads to 640 x 1408), a tall member and a square one,
+    all on the precise recipe (m < 4096)."""
+    shapes = [(512, 1024), (1300, 600), (512, 512)]
     wl = WL.custom(shapes, dtype=torch.bfloat16, g_std=1e-3, ns_steps=ns_steps, number=91)
     _banner(f"grouped steps, ns_steps={ns_steps}")
     res = run_and_compare(wl, steps=2) + ns_and_compare(wl)
     _banner(f"ns_steps={ns_steps}: worst O relF {max(r for r, _ in res):.3e}")
+
+
+@pytest.mark.parametrize("ns_steps", [10, 16])
+def test_many_ns_steps(ns_steps):
+    """The API's range of NS step counts up to 16: a matrix below m = 512
+    (all steps in one group with the split chain), square and wide ones on
+    the precise recipe (4 + pairs)."""
+    shapes = [(300, 300), (160, 700), (512, 512), (600, 1300)]
+    wl = WL.custom(shapes, dtype=torch.bfloat16, g_std=1e-3, ns_steps=ns_steps, number=92)
+    _banner(f"many steps, ns_steps={ns_steps}")
+    res = run_and_compare(wl, steps=2) + ns_and_compare(wl)
+    _banner(f"ns_steps={ns_steps}: worst O relF {max(r for r, _ in res):.3e}")
+
+
+def test_lean_recipe_sixteen_steps():
+    """m >= 4096 takes the lean recipe (single-product chain); [4096, 4096]
+    with the API's largest step count, through muon_ns and the step's O."""
+    wl = WL.custom([(4096, 4096)], dtype=torch.bfloat16, g_std=1e-3, ns_steps=16, number=93)
+    _banner("lean recipe, 16 steps")
+    res = ns_and_compare(wl)
+    _banner(f"4096^2, 16 steps: ns O relF {res[0][0]:.3e}")
 
 
 @pytest.mark.parametrize("nesterov", [False, True])

@@ -235,10 +235,9 @@ def executed_flops(wl) -> float:
     m >= 512, else three), after the group's first step the products
     T = P A, A' = P T and R = P R (m^3 each), and one apply 2 m^2 n.  The
     lo planes add products: the first Gram takes three (precise recipe,
-    m < 4096 or more than 5 steps), the chain products three each (precise),
-    and an apply one more
-    per lo plane it uses (X_0's in the first group, R's in the precise
-    recipe)."""
+    m < 4096 or more than 5 steps), the chain products three each (precise;
+    R one when m >= 1024 and N <= 5), and an apply one more per lo plane it
+    uses (X_0's in the first group, R's in the precise recipe)."""
     N = wl.ns_steps
     tot = 0.0
     for s in wl.shapes:
@@ -251,6 +250,7 @@ def executed_flops(wl) -> float:
         whole, precise = m < 512, (m < 4096 or N > 5)
         a2 = lambda k: (1 if (m >= 512 and k < min(3, N - 2)) else 3) * m ** 3  # noqa: E731
         chain = 3 if precise else 1
+        rprod = 1 if (not precise or (m >= 1024 and N <= 5)) else 3
         f, k = 0.0, 0
         while k < N:
             if whole:
@@ -261,7 +261,7 @@ def executed_flops(wl) -> float:
                 G = 2 if N - k >= 2 else 1
             gram = (3 if (k == 0 and precise) else 1) * m * m * n
             apply = (1 + (1 if k == 0 else 0) + (1 if precise else 0)) * 2 * m * m * n
-            f += gram + sum(a2(k + j) for j in range(G)) + 3 * chain * (G - 1) * m ** 3 + apply
+            f += gram + sum(a2(k + j) for j in range(G)) + (2 * chain + rprod) * (G - 1) * m ** 3 + apply
             k += G
         tot += b * f
     return tot

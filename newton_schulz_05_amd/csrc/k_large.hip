@@ -929,7 +929,8 @@ static inline bool split_a2(int64_t m, int k, int steps) {
 //     steps whose errors would be multiplied most;
 //   - the precise recipe (m < kLeanFromM, or more than kLeanMaxSteps steps)
 //     also splits the m x m chain: P, T and R carry lo planes and T, A' and
-//     R take the split products, and the apply uses the lo plane of R.
+//     R take the split products (R the single one from kRSingleFromM up, with
+//     at most kLeanMaxSteps steps), and the apply uses the lo plane of R.
 // See ns_recipe (plan.cpp) for which shapes take which recipe.
 template <int TILE, typename PT>
 static hipError_t ns_group_bf16(const LargeArgs& g, hipStream_t st, int k, int G, int cur, int last) {
@@ -994,7 +995,8 @@ static hipError_t ns_group_bf16(const LargeArgs& g, hipStream_t st, int k, int G
     const float* rd0 = (j == 1) ? Pdb[0] : Rdb[(j - 1) & 1];
     EpiPairR er{r0, cs ? r0l : nullptr, rd0, Pb[j & 1], cs ? PbL[j & 1] : nullptr, Pdb[j & 1],
                 Rb[j & 1], cs ? RbL[j & 1] : nullptr, Rdb[j & 1], scal, (k == 0 && j == 1) ? 1 : 0, mp};
-    if ((e = cs ? sym3(Pb[j & 1], PbL[j & 1], r0, r0l, er) : sym1(Pb[j & 1], r0, er)) != hipSuccess) return e;
+    const bool r3 = cs && !(g.m >= kRSingleFromM && steps <= kLeanMaxSteps);
+    if ((e = r3 ? sym3(Pb[j & 1], PbL[j & 1], r0, r0l, er) : sym1(Pb[j & 1], r0, er)) != hipSuccess) return e;
   }
   // apply with R (P_0 for a single step): A = R (+ its lo plane, precise),
   // B = Xt (+ X_0's lo plane)

@@ -133,9 +133,17 @@ int32_t mfma_tile(int64_t m, int64_t n, int64_t count);
 // [4096, 4096] reached 1.4e-2 on the GPU, the precise recipe 3.5e-3 at
 // [1024, 1024]); a call with more steps takes the precise chain, whose lo
 // planes every bf16 workspace therefore holds.
+// Within the precise recipe, R = P_j R_{j-1} takes the single product of
+// the hi planes (its epilogue still adds the diagonal terms with the lo
+// planes and writes R's lo plane) when m >= kRSingleFromM and the call has
+// at most kLeanMaxSteps steps: emulated on the same inputs, the rank-m/8
+// error rose from 5.7e-3 to 6.6e-3 at [1024, 2048] and from 5.0e-3 to
+// 5.8e-3 at [1536, 2048], but to 8.7e-3 at [512, 1024] and 2.5e-2 at
+// [64, 200] in a whole group, so smaller m keeps the split R.
 constexpr int64_t kWholeBelowM = 512;
 constexpr int64_t kLeanFromM = 4096;
 constexpr int kLeanMaxSteps = 5;
+constexpr int64_t kRSingleFromM = 1024;
 struct NsRecipe {
   bool whole, precise;
 };

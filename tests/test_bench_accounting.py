@@ -52,6 +52,22 @@ def test_executed_count_group_lengths(ns_steps, groups):
     assert bench.executed_flops(_wl([(m, n)], ns_steps)) == want
 
 
+@pytest.mark.parametrize("ns_steps,rprod", [(5, 1), (6, 3)])
+def test_executed_count_precise_r_single_from_1024(ns_steps, rprod):
+    # precise recipe at m = 1536 (the experts): T and A' split, R a single
+    # product up to 5 steps (three beyond); 5 steps as 4 + 1, 6 as 4 + 2
+    m, n = 1536, 2048
+    split = [k >= min(3, ns_steps - 2) for k in range(ns_steps)]
+    groups = [4, 1] if ns_steps == 5 else [4, 2]
+    want, k = 0, 0
+    for g in groups:
+        gram = (3 if k == 0 else 1) * m * m * n
+        apply = (3 if k == 0 else 2) * 2 * m * m * n
+        want += gram + sum((3 if split[k + j] else 1) * m ** 3 for j in range(g)) + (6 + rprod) * (g - 1) * m ** 3 + apply
+        k += g
+    assert bench.executed_flops(_wl([(n, m)], ns_steps)) == want
+
+
 def test_executed_count_whole_group_below_512():
     # m < 512: all 5 steps in one group, split A^2 everywhere, split chain,
     # first Gram and the one apply with both lo planes

@@ -40,7 +40,6 @@ namespace {
 
 constexpr int kNB = 8;            // 32-column blocks per wave (slab <= 4 * 8 * 32 = 1024 columns)
 constexpr int kLdr = 36;          // LDS column stride (bf16) of the Gram's restaging
-constexpr int kLdf = 36;          // LDS column stride (fp32) of the momentum block's staging
 constexpr int kPartW = 544;       // 8-byte words per published slab partial (upper triangle <= 528, + sum of squares)
 constexpr int kCoherent = 16;     // buffer cache policy: device-coherent access (sc1)
 constexpr int kGather = 12;       // partial words each thread has in flight while gathering
@@ -48,31 +47,31 @@ constexpr int kGather = 12;       // partial words each thread has in flight whi
 __device__ __forceinline__ int row_of(int r, int h) { return ((r >> 2) << 3) + (h << 2) + (r & 3); }
 
 // In muon_step the NS input U (fp32) is held as hi = bf16(U) in registers
-// and its remainder lo = U - hi (exact in fp32) as an 8-bit code against
-// hi's exponent E: code = round(lo * 2^(15 - E)), lo ~ code * 2^(E - 15).
-// |lo| is at most half an ulp of hi, 2^(E - 8), so |code| <= 128 (clamped
-// to 127) and the code carries 8 more bits of U: hi + lo holds U to about
-// 2^-16 relative.  The decoded lo is exactly a bf16 value.  Hi below 2^-111
-// (or not finite) gets code 0.
+// and its remainder lo = U - hi as an 8-bit code.  The code is the
+// difference of the fp32 bit patterns of U and of hi (hi's pattern is its
+// bf16 bits times 2^16), an integer d with |d| <= 2^15 since U rounds to the
+// nearest hi (the patterns of same-signed floats are monotonic, across
+// binades too), rounded to a multiple of 2^8: code = floor((d + 128) / 2^8),
+// clamped to 127.  The decoded value is the float whose pattern is hi's plus
+// code * 2^8, i.e. U with its 8 lowest mantissa bits rounded away, and
+// lo = that - hi is exact and exactly a bf16 value (at most 8 significant
+// bits).  hi + lo holds U to about 2^-16 relative.  A zero, subnormal or
+// non-finite hi decodes to lo = 0 whatever the code (the codes of padding
+// rows are not written).
 __device__ __forceinline__ uint32_t lo_code(float u, uint32_t hi) {
-  const uint32_t ef = (hi >> 7) & 0xffu;
-  const bool ok = ef - 16u <= 238u;                                         // 16 <= ef <= 254
-  const float lo = u - __uint_as_float(hi << 16);
-  const float scale = __uint_as_float((269u << 23) - ((hi << 16) & 0x7f800000u));  // 2^(15 - E)
-  const float c = __builtin_amdgcn_fmed3f(rintf(lo * scale), -127.f, 127.f);
-  return ok ? (uint32_t(int(c)) & 0xffu) : 0u;
+  const int d = int(__float_as_uint(u) - (hi << 16));
+  const int c = (d + 128) >> 8;  // >= -128
+  return uint32_t(c < 127 ? c : 127) & 0xffu;
 }
 // lo (as bf16 bits) of the value whose hi is `hi` and whose code is the
-// byte `code` (bits 0-7): code * 2^(E - 15), the code carrying lo's sign;
-// 0 for hi below 2^-111
+// byte `code` (bits 0-7)
 __device__ __forceinline__ uint32_t lo_decode(uint32_t hi, uint32_t code) {
-  const uint32_t ex = (hi << 16) & 0x7f800000u;        // exponent of hi, fp32 position
-  const bool ok = (ex >> 23) > 15u;
-  const float scale = __uint_as_float(ex - (15u << 23));  // 2^(E - 15)
-  // the byte as a signed value by a shift pair (the form sbfe + conversion
-  // was lowered to an unsigned conversion of the sign-extended byte)
-  const float v = float(int(code << 24) >> 24) * scale;
-  return ok ? uint32_t(f2bf(v)) : 0u;
+  const uint32_t h = hi << 16;
+  // code * 2^8, sign-extended from the byte by a shift pair
+  const uint32_t dd = uint32_t(int(code << 24) >> 16);
+  const float v = __uint_as_float(h + dd) - __uint_as_float(h);
+  const uint32_t ef = (h >> 23) & 0xffu;
+  return (ef - 1u < 254u) ? uint32_t(f2bf(v)) : 0u;
 }
 // codes of the 16 values of a lane's block (U in u, hi in the bf16 pairs
 // x), value r in byte r % 4 of word r / 4

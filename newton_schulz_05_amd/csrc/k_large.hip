@@ -594,6 +594,53 @@ __device__ __forceinline__ void tile_coords(int t, int T, bool upper, int& ti, i
   ti = r; tj = r + t;
 }
 
+// Workgroup b of a launch of N runs on XCD b mod 8, and each XCD takes its
+// workgroups in order.  Work item of b: each XCD gets a contiguous range of
+// the items (the last N mod 8 workgroups take the items left over), so the
+// items an XCD runs together are neighbours and share operand blocks in its
+// L2.  With the grouped tile orders below, the 8192 x 28672 pair's step
+// went from 53.5 to 52.2 ms and the MoE experts' from 3.37 to 2.96 ms.
+__device__ __forceinline__ int xcd_item(int b, int N) {
+  const int nx = N >> 3;
+  return (b < 8 * nx) ? (b & 7) * nx + (b >> 3) : b;
+}
+// Tile (ti, tj) of item t of a Tm x Tn grid in column-major groups of kGM
+// tile rows: the tiles that run together share kGM row blocks of A and a
+// few column blocks of B.
+constexpr int kGM = 4;
+__device__ __forceinline__ void grouped_coords(int t, int Tm, int Tn, int& ti, int& tj) {
+  const int g = t / (kGM * Tn), w = t - g * (kGM * Tn);
+  const int gm = (Tm - g * kGM < kGM) ? Tm - g * kGM : kGM;
+  ti = g * kGM + w % gm;
+  tj = w / gm;
+}
+// The same for the upper triangle (i <= j) of a T x T grid: groups of kGM
+// tile rows r0 .. r0+gm-1, each taken column by column from j = r0 (the
+// first gm - 1 columns hold 1, 2, .. gm - 1 tiles of the group).
+__device__ __forceinline__ void grouped_upper_coords(int t, int T, int& ti, int& tj) {
+  int r0 = 0;
+  for (;;) {
+    const int gm = (T - r0 < kGM) ? T - r0 : kGM;
+    const int size = gm * (T - r0) - gm * (gm - 1) / 2;
+    if (t < size) {
+      const int tri = gm * (gm - 1) / 2;
+      if (t < tri) {
+        int jj = 0;
+        while ((jj + 1) * (jj + 2) / 2 <= t) ++jj;
+        ti = r0 + (t - jj * (jj + 1) / 2);
+        tj = r0 + jj;
+      } else {
+        const int w = t - tri;
+        ti = r0 + w % gm;
+        tj = r0 + gm - 1 + w / gm;
+      }
+      return;
+    }
+    t -= size;
+    r0 += gm;
+  }
+}
+
 // ============================================================================
 // bf16 MFMA GEMM, "NT": C[i][j] = sum_k A[i][k] * B[j][k] (+ split products)
 // A, B row-major with k contiguous; all dims padded to the tile size.
@@ -655,13 +702,15 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
   constexpr int KS = BK / 16;
   __shared__ u16x8 lds[2][NPL][PLANE];          // [stage][Ah, (Al), Bh, (Bl)]
   // Work item f = matrix * per + tile, in units of the tiles that tilesN
-  // counts.  With split, each such tile (twice TILE on a side) is done by four
-  // workgroups, one per TILE-quarter; a symmetric output skips the quarter
-  // below the diagonal.
-  const int f = base + (split ? int(blockIdx.x >> 2) : int(blockIdx.x));
+  // counts, tiles in the grouped order (which only decides which workgroup
+  // computes a tile, never how).  With split, each such tile (twice TILE on a
+  // side) is done by four workgroups, one per TILE-quarter; a symmetric
+  // output skips the quarter below the diagonal.
+  const int f = base + (split ? int(blockIdx.x >> 2) : xcd_item(int(blockIdx.x), int(gridDim.x)));
   const int z = f / per;
   int ti, tj;
-  tile_coords(f - z * per, tilesN, upper != 0, ti, tj);
+  if (upper) grouped_upper_coords(f - z * per, tilesN, ti, tj);
+  else grouped_coords(f - z * per, per / tilesN, tilesN, ti, tj);
   if (split) {
     const int q = int(blockIdx.x & 3);
     ti = 2 * ti + (q >> 1);

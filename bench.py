@@ -28,18 +28,22 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 
 
-# HBM traffic of the skinny kernel on the 74 x [24, 10240] workload, from two
-# rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean
-# over the profiled dispatches), each scaled by the ratio of known bytes to
-# the same counter on a plain device copy (`bench.py --copy-probe`).  Valid
-# only for the kernel source it was taken on (SHA-256 of k_skinny.hip);
-# otherwise `traffic` is reported as null.
-SKINNY_TRAFFIC = {
-    "kernel_source_sha256": "98284fed7dda61e39386a336ed8957e3b30cc7eb74cea5b2512e3e5798d09510",
-    "fetch_kib_per_dispatch": 83141.0,
-    "write_kib_per_dispatch": 109317.9,
-    "fetch_scale": 2.0,      # 262144 KiB copied / 131085.5 KiB counted
-    "write_scale": 1.0,      # 262144 KiB copied / 262144.0 KiB counted
+# HBM traffic per launch of a workload's dominant kernel (the one its
+# roofline object names), from two rocprofv3 --pmc runs (FETCH_SIZE, then
+# WRITE_SIZE; KiB per dispatch, mean over the profiled dispatches of that
+# kernel), each scaled by the ratio of known bytes to the same counter on a
+# plain device copy (`bench.py --copy-probe`: 262144 KiB copied, FETCH_SIZE
+# 131085 KiB, WRITE_SIZE 262144 KiB).  Valid only for the kernel source it
+# was taken on (SHA-256); otherwise `traffic` is reported as null.
+TRAFFIC = {
+    "c2": {"source": "k_skinny.hip",
+           "kernel_source_sha256": "de1e80a431de6622585be7aa758452062d9b18ccfca13aafbfe7406fd5fe82f5",
+           "fetch_kib_per_dispatch": 83727.4, "write_kib_per_dispatch": 109375.8,
+           "fetch_scale": 2.0, "write_scale": 1.0},
+    "c5": {"source": "k_large.hip",
+           "kernel_source_sha256": "8ef06319815fea0d0b04c873f57aac098d6a0a1b34807e8340e1b2039a1c780c",
+           "fetch_kib_per_dispatch": 12058712.5, "write_kib_per_dispatch": 1553929.8,
+           "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 
@@ -50,9 +54,9 @@ def _kernel_sha(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def skinny_traffic_bytes():
-    t = SKINNY_TRAFFIC
-    if t["kernel_source_sha256"] is None or t["kernel_source_sha256"] != _kernel_sha("k_skinny.hip"):
+def traffic_bytes(key: str):
+    t = TRAFFIC.get(key)
+    if t is None or t["kernel_source_sha256"] is None or t["kernel_source_sha256"] != _kernel_sha(t["source"]):
         return None
     return 1024.0 * (t["fetch_kib_per_dispatch"] * t["fetch_scale"] + t["write_kib_per_dispatch"] * t["write_scale"])
 
@@ -385,7 +389,7 @@ def _roofline(wl, res):
     ms = res["ms"]
     if all(g["m"] <= 32 for g in res["plan"]) and wl.dtype == torch.bfloat16:
         gbs = alg_bytes(wl) / (ms * 1e-3) / 1e9
-        tr = skinny_traffic_bytes() if wl.key == "c2" else None
+        tr = traffic_bytes(wl.key)
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None if tr is None else round(tr),
                 "kernel": "skinny_kernel", "launches_per_step": sum(g["n_chunks"] for g in res["plan"])}
@@ -402,8 +406,9 @@ def _roofline(wl, res):
     plain = kt["alg_flops"] / (kt["ms"] * 1e-3) / 1e12
     steps = max(1, res.get("steps", 1))
     n = max(1, kt["launches"])
+    tr = traffic_bytes(wl.key)
     return {"bound": "mfma", "achieved": round(ex, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(ex / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "frac": round(ex / BF16_PEAK_TFLOPS, 4), "traffic": None if tr is None else round(tr),
             "kernel": "gemm_bf16_kernel<*, *, EpiApplyBf16> (apply X' = R X)",
             "launches_per_step": round(kt["launches"] / steps, 2),
             "avg_launch_ms": round(kt["ms"] / n, 4),

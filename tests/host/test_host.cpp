@@ -93,7 +93,7 @@ static void test_workload_plans() {
   CHECK(p2.groups.size() == 1 && p2.groups[0].path == PATH_SKINNY && p2.groups[0].slabs == 10);
   Plan p3 = make({{8, 2048, 1536}, {32, 24, 10240}});
   check_plan(p3);
-  CHECK(p3.groups.size() == 2 && p3.groups[0].n_tr == 8 && p3.groups[0].tile == 128);
+  CHECK(p3.groups.size() == 2 && p3.groups[0].n_tr == 8 && p3.groups[0].tile == 256);
   std::vector<muon_shape> c4;
   for (int l = 0; l < 32; ++l) {
     for (int q = 0; q < 4; ++q) c4.push_back({1, 4096, 4096});

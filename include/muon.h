@@ -103,7 +103,9 @@ typedef struct muon_plan_s* muon_plan;
  *   out       : receives the plan.
  * Matrices are grouped by (min(rows,cols), max(rows,cols)); tall matrices
  * (rows > cols) join the group of their transpose and are handled in the wide
- * orientation.  No HIP call is made: the device is first queried (compute
+ * orientation.  MUON_ERR_SHAPE for a dimension < 1, a matrix of more than
+ * 2^40 elements, or a bf16 matrix on the MFMA path (min > 32, or too wide
+ * for the skinny path) with max(rows, cols) > 2^22 - 256.  No HIP call is made: the device is first queried (compute
  * units, co-resident capacity) by the first muon_step / muon_ns on it. */
 muon_status muon_plan_create(const muon_shape* shapes, int32_t n_params, muon_dtype param_dt,
                              muon_dtype grad_dt, muon_dtype mom_dt, muon_plan* out);

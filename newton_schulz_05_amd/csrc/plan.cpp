@@ -200,6 +200,11 @@ muon_status build_plan(const muon_shape* shapes, int32_t n_params, muon_dtype pa
       g.path = PATH_SKINNY;
     } else {
       g.path = PATH_MFMA;
+      if (g.n > kMfmaMaxN) {
+        *detail = "bf16 matrices with min(rows, cols) > 32 (or too wide for the skinny path) are limited to "
+                  "max(rows, cols) <= " + std::to_string(kMfmaMaxN);
+        return MUON_ERR_SHAPE;
+      }
     }
     if (g.path == PATH_SKINNY) {
       g.slabs = (int32_t)ceil_div(g.n, kSkinnyMaxSlab);

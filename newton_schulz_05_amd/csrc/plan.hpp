@@ -26,6 +26,10 @@ enum Path : int32_t {
 
 // Geometry constants the kernels are compiled for.
 constexpr int64_t kSkinnyMaxM = 32;          // rows of the padded MFMA tile
+// Largest n of a bf16 MFMA-path group: a 256-row operand tile of the padded
+// row length (< 2^22 elements) spans less than 2^31 bytes, the range of the
+// 32-bit buffer offsets its loads use.
+constexpr int64_t kMfmaMaxN = (int64_t(1) << 22) - 256;
 constexpr int64_t kSkinnyBlocksPerWave = 8;  // 32-column blocks each wave keeps in registers
 constexpr int64_t kSkinnyWaves = 4;
 constexpr int64_t kSkinnyMaxSlab = 32 * kSkinnyBlocksPerWave * kSkinnyWaves;  // 1024 columns

@@ -79,6 +79,22 @@ def test_bad_shapes_rejected(shape):
     assert e.value.name == "MUON_ERR_SHAPE"
 
 
+def test_mfma_width_limit():
+    """bf16 MFMA-path groups address a 256-row operand tile with 32-bit
+    buffer offsets, so max(rows, cols) is limited to 2^22 - 256 there (tall
+    members too; a matrix that wide is also beyond the skinny path's
+    co-resident slabs whatever its m); fp32 keeps wider matrices."""
+    lim = (1 << 22) - 256
+    MuonPlan([(64, lim)], torch.bfloat16)
+    for shape in [(64, lim + 1), (lim + 1, 64)]:
+        with pytest.raises(MuonError) as e:
+            MuonPlan([shape], torch.bfloat16)
+        assert e.value.name == "MUON_ERR_SHAPE"
+    with pytest.raises(MuonError):
+        MuonPlan([(24, lim + 1)], torch.bfloat16)
+    MuonPlan([(64, lim + 1)], torch.float32)
+
+
 def test_one_d_rejected():
     with pytest.raises(MuonError) as e:
         MuonPlan([(5,)], torch.bfloat16)

@@ -41,8 +41,8 @@ TRAFFIC = {
            "fetch_kib_per_dispatch": 83727.4, "write_kib_per_dispatch": 109375.8,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
-           "kernel_source_sha256": "8ef06319815fea0d0b04c873f57aac098d6a0a1b34807e8340e1b2039a1c780c",
-           "fetch_kib_per_dispatch": 12058712.5, "write_kib_per_dispatch": 1553929.8,
+           "kernel_source_sha256": "034d7c2e6f94f2fecef5806da0850929b59f8c363d3531812e6543d4083d47cc",
+           "fetch_kib_per_dispatch": 11983334.3, "write_kib_per_dispatch": 1548857.5,
            "fetch_scale": 2.0, "write_scale": 1.0},
 }
 

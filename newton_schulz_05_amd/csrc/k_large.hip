@@ -220,6 +220,18 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ nor
 // so that every store is a run of 16 consecutive elements (16-byte vectors
 // where aligned).  `diag` is true on tiles on the diagonal of a symmetric
 // output, where only i <= j is owned by the row pass and i < j is mirrored.
+// Memory reads happen outside row() and col(), so that no read waits behind
+// the stores of an earlier sub-tile (the vector memory counter retires loads
+// and stores in issue order, so a wait for a load is a wait for every older
+// store):
+//   uni(z)                        the matrix's values (scale factors, the
+//                                 stored orientation), once per tile before
+//                                 any store;
+//   fetch(u, z, i, j0, j, i0, in) the sub-tile's inputs (runs of the
+//                                 operands, per-row values), issued one
+//                                 sub-tile ahead.  Full runs are loaded even
+//                                 on diagonal tiles; the entries below the
+//                                 diagonal are not used.
 // fp32 path: the GEMM hands a run of 4 consecutive rows (i0 .. i0+3) of one
 // column j.
 // ============================================================================
@@ -279,6 +291,31 @@ template <> struct Seg<uint16_t> {
 
 __device__ __forceinline__ int clamp16(int64_t x) { return x <= 0 ? 0 : (x >= 16 ? 16 : int(x)); }
 
+// 16 consecutive elements held as loaded (16-byte vectors, not yet
+// converted), so that an epilogue issues the loads of a sub-tile before the
+// stores of the previous one and waits for them only where it uses them.
+// The address must be 16-byte aligned.
+template <typename T> struct Run;
+template <> struct Run<float> {
+  f32x4 q[4];
+  __device__ __forceinline__ void fetch(const float* p) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = ((const f32x4*)p)[k];
+  }
+  __device__ __forceinline__ float operator[](int k) const { return q[k >> 2][k & 3]; }
+};
+template <> struct Run<uint16_t> {
+  u32x4 q[2];
+  __device__ __forceinline__ void fetch(const uint16_t* p) {
+    q[0] = ((const u32x4*)p)[0];
+    q[1] = ((const u32x4*)p)[1];
+  }
+  __device__ __forceinline__ float operator[](int k) const {
+    const uint32_t w = q[k >> 3][(k >> 1) & 3];
+    return bf2f(uint16_t((k & 1) ? (w >> 16) : (w & 0xffffu)));
+  }
+};
+
 struct NatStore {
   // store O (fp32) or apply the weight update at the matrix's stored position
   template <typename PT>
@@ -295,10 +332,11 @@ struct NatStore {
       Elem<PT>::store(W + idx, fmaf(-sc.lr * sc.scale, o, w * keep));
     }
   }
-  // the same for `cnt` consecutive stored elements starting at idx0
+  // the same for `cnt` consecutive stored elements starting at idx0; `pre`,
+  // when given, holds the 16 W values already loaded (cnt == 16)
   template <typename PT>
   __device__ static __forceinline__ void put_seg(const MatRef& r, const StepScalars& sc, int64_t idx0, int cnt,
-                                                 const float* o) {
+                                                 const float* o, const Run<PT>* pre = nullptr) {
     if (cnt <= 0) return;
     if (sc.mode == 1) {
       Seg<float>::store((float*)r.w + idx0, 0, cnt, o);
@@ -306,7 +344,12 @@ struct NatStore {
     }
     PT* W = (PT*)r.w + idx0;
     float w[16] = {};
-    Seg<PT>::load(W, 0, cnt, w);
+    if (pre) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) w[k] = (*pre)[k];
+    } else {
+      Seg<PT>::load(W, 0, cnt, w);
+    }
     const float keep = 1.0f - sc.lr * sc.wd;
 #pragma unroll
     for (int k = 0; k < 16; ++k) w[k] = fmaf(-sc.lr * sc.scale, o[k], w[k] * keep);
@@ -321,8 +364,13 @@ struct NatStore {
 struct EpiGramBf16 {
   float* A; uint16_t* H; uint16_t* L; const float* scal; int use_scale; int with_lo; int64_t mp;
   static constexpr bool kCol = true;
-  __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool diag) const {
-    const float s2 = use_scale ? scal[z * 4 + 1] : 1.0f;
+  struct Uni { float s2; };
+  struct In {};
+  __device__ __forceinline__ Uni uni(int z) const { return Uni{use_scale ? scal[z * 4 + 1] : 1.0f}; }
+  __device__ __forceinline__ void fetch(const Uni&, int, int64_t, int64_t, int64_t, int64_t, In&) const {}
+  __device__ __forceinline__ void row(const Uni& un, int z, int64_t i, int64_t j0, float* v, bool diag,
+                                      const In&) const {
+    const float s2 = un.s2;
     float lo[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -335,7 +383,8 @@ struct EpiGramBf16 {
     Seg<uint16_t>::store(H + o, k0, 16, v);
     if (with_lo) Seg<uint16_t>::store(L + o, k0, 16, lo);
   }
-  __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
+  __device__ __forceinline__ void col(const Uni&, int z, int64_t j, int64_t i0, const float* v, bool diag,
+                                      const In&) const {
     float lo[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
@@ -352,15 +401,21 @@ struct EpiPolyBf16 {
   const float* A; uint16_t* Poff; uint16_t* PoffL; float* Pd; const float* scal; int use_scale;
   float a, b, c; int64_t mp, m;
   static constexpr bool kCol = true;
-  __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool diag) const {
-    const float ps = use_scale ? scal[z * 4 + 0] : 1.0f;
+  struct Uni { float ps; };
+  struct In { Run<float> a; };
+  __device__ __forceinline__ Uni uni(int z) const { return Uni{use_scale ? scal[z * 4 + 0] : 1.0f}; }
+  __device__ __forceinline__ void fetch(const Uni&, int z, int64_t i, int64_t j0, int64_t, int64_t, In& in) const {
+    in.a.fetch(A + int64_t(z) * mp * mp + i * mp + j0);
+  }
+  __device__ __forceinline__ void row(const Uni& un, int z, int64_t i, int64_t j0, float* v, bool diag,
+                                      const In& in) const {
+    const float ps = un.ps;
     const int k0 = diag ? clamp16(i - j0) : 0;
     const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
-    float av[16] = {}, pv[16];
-    Seg<float>::load(A + o, k0, 16, av);  // positions below k0 are not used
+    float pv[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      float p = fmaf(c, v[k], b * av[k]);
+      float p = fmaf(c, v[k], b * in.a[k]);
       if (i == j0 + k) {
         p = ps * (p + a);
         Pd[int64_t(z) * mp + i] = (i < m) ? p : 0.f;
@@ -379,7 +434,8 @@ struct EpiPolyBf16 {
       Seg<uint16_t>::store(PoffL + o, k0, 16, lo);
     }
   }
-  __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
+  __device__ __forceinline__ void col(const Uni&, int z, int64_t j, int64_t i0, const float* v, bool diag,
+                                      const In&) const {
     const int k1 = diag ? clamp16(j - i0) : 16;
     const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
     Seg<uint16_t>::store(Poff + o, 0, k1, v);
@@ -401,22 +457,29 @@ struct EpiPolyBf16 {
 struct EpiSymMul {
   float* S; const float* d; uint16_t* H; uint16_t* L; int with_lo; int64_t mp;
   static constexpr bool kCol = true;
-  __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool diag) const {
+  struct Uni {};
+  struct In { Run<float> s; float d; };
+  __device__ __forceinline__ Uni uni(int) const { return Uni{}; }
+  __device__ __forceinline__ void fetch(const Uni&, int z, int64_t i, int64_t j0, int64_t, int64_t, In& in) const {
+    in.s.fetch(S + int64_t(z) * mp * mp + i * mp + j0);
+    in.d = d[int64_t(z) * mp + i];
+  }
+  __device__ __forceinline__ void row(const Uni&, int z, int64_t i, int64_t j0, float* v, bool diag,
+                                      const In& in) const {
     const int k0 = diag ? clamp16(i - j0) : 0;  // diagonal tiles: j >= i
     const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
-    float sv[16] = {}, lo[16];
-    Seg<float>::load(S + o, k0, 16, sv);
-    const float di = d[int64_t(z) * mp + i];
+    float lo[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      v[k] = fmaf(di, sv[k], v[k]);
+      v[k] = fmaf(in.d, in.s[k], v[k]);
       lo[k] = v[k] - bf2f(f2bf(v[k]));
     }
     Seg<float>::store(S + o, k0, 16, v);
     Seg<uint16_t>::store(H + o, k0, 16, v);
     if (with_lo) Seg<uint16_t>::store(L + o, k0, 16, lo);
   }
-  __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
+  __device__ __forceinline__ void col(const Uni&, int z, int64_t j, int64_t i0, const float* v, bool diag,
+                                      const In&) const {
     const int k1 = diag ? clamp16(j - i0) : 16;  // diagonal tiles: mirror i < j only
     const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
     Seg<uint16_t>::store(H + o, 0, k1, v);
@@ -441,32 +504,36 @@ struct EpiPairR {
   const uint16_t* Poff1; const uint16_t* Poff1L; const float* Pd1;
   uint16_t* Roff; uint16_t* RoffL; float* Rd; const float* scal; int use_scale; int64_t mp;
   static constexpr bool kCol = true;
-  __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool diag) const {
-    const float ps = use_scale ? scal[z * 4 + 0] : 1.0f;
+  // its inputs are too many registers to hold for two sub-tiles at once:
+  // they are fetched just before their sub-tile
+  static constexpr bool kAhead = false;
+  struct Uni { float ps; };
+  struct In { Run<uint16_t> p0, p1, p0l, p1l; Run<float> d0; float d1; };
+  __device__ __forceinline__ Uni uni(int z) const { return Uni{use_scale ? scal[z * 4 + 0] : 1.0f}; }
+  __device__ __forceinline__ void fetch(const Uni&, int z, int64_t i, int64_t j0, int64_t, int64_t, In& in) const {
+    const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
+    in.p0.fetch(Poff0 + o);
+    in.p1.fetch(Poff1 + o);
+    if (Poff0L) in.p0l.fetch(Poff0L + o);
+    if (Poff1L) in.p1l.fetch(Poff1L + o);
+    in.d0.fetch(Pd0 + int64_t(z) * mp + j0);
+    in.d1 = Pd1[int64_t(z) * mp + i];
+  }
+  __device__ __forceinline__ void row(const Uni& un, int z, int64_t i, int64_t j0, float* v, bool diag,
+                                      const In& in) const {
+    const float ps = un.ps;
     const int k0 = diag ? clamp16(i - j0) : 0;
     const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
-    float p0[16] = {}, p1[16] = {}, d0[16] = {}, rv[16];
-    Seg<uint16_t>::load(Poff0 + o, k0, 16, p0);
-    Seg<uint16_t>::load(Poff1 + o, k0, 16, p1);
-    if (Poff0L) {
-      float l[16] = {};
-      Seg<uint16_t>::load(Poff0L + o, k0, 16, l);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) p0[k] += l[k];
-    }
-    if (Poff1L) {
-      float l[16] = {};
-      Seg<uint16_t>::load(Poff1L + o, k0, 16, l);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) p1[k] += l[k];
-    }
-    Seg<float>::load(Pd0 + int64_t(z) * mp + j0, k0, 16, d0);
-    const float d1 = Pd1[int64_t(z) * mp + i];
+    float rv[16];
+    const float d1 = in.d1;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      float r = fmaf(d1, p0[k], fmaf(p1[k], d0[k], v[k]));
+      const float p0 = Poff0L ? in.p0[k] + in.p0l[k] : in.p0[k];
+      const float p1 = Poff1L ? in.p1[k] + in.p1l[k] : in.p1[k];
+      const float d0 = in.d0[k];
+      float r = fmaf(d1, p0, fmaf(p1, d0, v[k]));
       if (i == j0 + k) {
-        r = ps * fmaf(d1, d0[k], r);
+        r = ps * fmaf(d1, d0, r);
         Rd[int64_t(z) * mp + i] = r;
         rv[k] = 0.f;
       } else {
@@ -483,7 +550,8 @@ struct EpiPairR {
       Seg<uint16_t>::store(RoffL + o, k0, 16, lo);
     }
   }
-  __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool diag) const {
+  __device__ __forceinline__ void col(const Uni&, int z, int64_t j, int64_t i0, const float* v, bool diag,
+                                      const In&) const {
     const int k1 = diag ? clamp16(j - i0) : 16;
     const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
     Seg<uint16_t>::store(Roff + o, 0, k1, v);
@@ -504,30 +572,49 @@ struct EpiApplyBf16 {
   MatTable tab; StepScalars sc; uint16_t* X; const uint16_t* Xl; uint16_t* XtN; const float* Pd;
   int64_t mp, np, m, n; int last;
   static constexpr bool kCol = true;
-  __device__ __forceinline__ void row(int z, int64_t i, int64_t j0, float* v, bool) const {
-    uint16_t* Xr = X + int64_t(z) * mp * np + i * np + j0;
-    float x[16];
-    Seg<uint16_t>::load(Xr, 0, 16, x);
-    if (Xl) {
-      float l[16];
-      Seg<uint16_t>::load(Xl + int64_t(z) * mp * np + i * np + j0, 0, 16, l);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) x[k] += l[k];
-    }
-    const float d = Pd[int64_t(z) * mp + i];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = fmaf(d, x[k], v[k]);
-    if (!last) {
-      Seg<uint16_t>::store(Xr, 0, 16, v);
-    } else if (!tab.tr[z]) {
-      NatStore::put_seg<PT>(tab.e[z], sc, i * n + j0, (i < m) ? clamp16(n - j0) : 0, v);
+  // the matrix's stored orientation and W; per sub-tile X's run (hi and lo
+  // planes), Pd[i], and on the last step the W run the update reads (the row
+  // run for a member stored as is, the column run for a transposed one) when
+  // it is whole and 16-byte aligned (otherwise the update loads W itself)
+  struct Uni { MatRef e; int tr; };
+  struct In { Run<uint16_t> x, xl; float d; Run<PT> w; int64_t widx; int wcnt; bool wpre; };
+  __device__ __forceinline__ Uni uni(int z) const { return Uni{tab.e[z], tab.tr[z] != 0}; }
+  __device__ __forceinline__ void fetch(const Uni& un, int z, int64_t i, int64_t j0, int64_t jc, int64_t ic,
+                                        In& in) const {
+    const int64_t o = int64_t(z) * mp * np + i * np + j0;
+    in.x.fetch(X + o);
+    if (Xl) in.xl.fetch(Xl + o);
+    in.d = Pd[int64_t(z) * mp + i];
+    in.wpre = false;
+    if (last) {
+      if (!un.tr) {
+        in.widx = i * n + j0;
+        in.wcnt = (i < m) ? clamp16(n - j0) : 0;
+      } else {
+        in.widx = jc * m + ic;
+        in.wcnt = (jc < n) ? clamp16(m - ic) : 0;
+      }
+      const PT* W = (const PT*)un.e.w + in.widx;
+      in.wpre = sc.mode != 1 && in.wcnt == 16 && ((uintptr_t)W & 15) == 0;
+      if (in.wpre) in.w.fetch(W);
     }
   }
-  __device__ __forceinline__ void col(int z, int64_t j, int64_t i0, const float* v, bool) const {
+  __device__ __forceinline__ void row(const Uni& un, int z, int64_t i, int64_t j0, float* v, bool,
+                                      const In& in) const {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = fmaf(in.d, Xl ? in.x[k] + in.xl[k] : in.x[k], v[k]);
+    if (!last) {
+      Seg<uint16_t>::store(X + int64_t(z) * mp * np + i * np + j0, 0, 16, v);
+    } else if (!un.tr) {
+      NatStore::put_seg<PT>(un.e, sc, in.widx, in.wcnt, v, in.wpre ? &in.w : nullptr);
+    }
+  }
+  __device__ __forceinline__ void col(const Uni& un, int z, int64_t j, int64_t i0, const float* v, bool,
+                                      const In& in) const {
     if (!last) {
       Seg<uint16_t>::store(XtN + int64_t(z) * mp * np + j * mp + i0, 0, 16, v);
-    } else if (tab.tr[z]) {
-      NatStore::put_seg<PT>(tab.e[z], sc, j * m + i0, (j < n) ? clamp16(m - i0) : 0, v);
+    } else if (un.tr) {
+      NatStore::put_seg<PT>(un.e, sc, in.widx, in.wcnt, v, in.wpre ? &in.w : nullptr);
     }
   }
 };
@@ -669,6 +756,11 @@ __device__ __forceinline__ void grouped_upper_coords(int t, int T, int& ti, int&
 // that of two at BK = 64.
 constexpr int kHH = 1, kHL = 2, kLH = 4;
 
+// whether an epilogue's inputs are fetched one sub-tile ahead (the default)
+// or just before their sub-tile (Epi::kAhead = false)
+template <typename Epi, typename = void> struct EpiAhead { static constexpr bool value = true; };
+template <typename Epi> struct EpiAhead<Epi, decltype(void(Epi::kAhead))> { static constexpr bool value = Epi::kAhead; };
+
 template <int TILE>
 struct GemmGeom {
   static constexpr int NT = (TILE == 256) ? 512 : 256;
@@ -714,7 +806,7 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
   // side) is done by four workgroups, one per TILE-quarter; a symmetric
   // output skips the quarter below the diagonal.
   const int f = base + (split ? int(blockIdx.x >> 2) : xcd_item(int(blockIdx.x), int(gridDim.x)));
-  const int z = f / per;
+  const int z = __builtin_amdgcn_readfirstlane(f / per);
   int ti, tj;
   if (upper) grouped_upper_coords(f - z * per, tilesN, ti, tj);
   else grouped_coords(f - z * per, per / tilesN, tilesN, ti, tj);
@@ -840,25 +932,40 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
   float* slot = reinterpret_cast<float*>(&lds[0][0][0]) + wv * (32 * kLd);
   const bool diag = upper && (ti == tj);
   const int er = lane >> 1, ec = (lane & 1) * 16;
+  // the matrix's values once, then the wave's MFMA tiles in order, each
+  // one's inputs fetched one tile ahead
+  const typename Epi::Uni un = epi.uni(z);
+  constexpr int NTL = G::FM * G::FN;
+  typename Epi::In in[2];
+  auto fetch = [&](int u, typename Epi::In& dst) {
+    const int64_t ti0 = row0 + wr + (u / G::FN) * 32, tj0 = col0 + wc + (u % G::FN) * 32;
+    epi.fetch(un, z, ti0 + er, tj0 + ec, tj0 + er, ti0 + ec, dst);
+  };
+  constexpr bool ahead = EpiAhead<Epi>::value;
+  if (ahead) fetch(0, in[0]);
 #pragma unroll
-  for (int a = 0; a < G::FM; ++a)
-#pragma unroll
-    for (int b = 0; b < G::FN; ++b) {
-      const int64_t ti0 = row0 + wr + a * 32, tj0 = col0 + wc + b * 32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) slot[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kLd + (lane & 31)] = acc[a][b][r];
-      float v[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = slot[er * kLd + ec + k];
-      epi.row(z, ti0 + er, tj0 + ec, v, diag);
-      if constexpr (Epi::kCol) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) slot[er * kLd + ec + k] = v[k];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = slot[(ec + k) * kLd + er];
-        epi.col(z, tj0 + er, ti0 + ec, v, diag);
-      }
+  for (int u = 0; u < NTL; ++u) {
+    if (ahead) {
+      if (u + 1 < NTL) fetch(u + 1, in[(u + 1) & 1]);
+    } else {
+      fetch(u, in[u & 1]);
     }
+    const int a = u / G::FN, b = u % G::FN;
+    const int64_t ti0 = row0 + wr + a * 32, tj0 = col0 + wc + b * 32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) slot[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kLd + (lane & 31)] = acc[a][b][r];
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = slot[er * kLd + ec + k];
+    epi.row(un, z, ti0 + er, tj0 + ec, v, diag, in[u & 1]);
+    if constexpr (Epi::kCol) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) slot[er * kLd + ec + k] = v[k];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = slot[(ec + k) * kLd + er];
+      epi.col(un, z, tj0 + er, ti0 + ec, v, diag, in[u & 1]);
+    }
+  }
 }
 
 // ============================================================================

@@ -788,7 +788,7 @@ template <int TILE, int PR, typename Epi>
 __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void gemm_bf16_kernel(
     const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al, int64_t lda, int64_t sA,
     const uint16_t* __restrict__ Bh, const uint16_t* __restrict__ Bl, int64_t ldb, int64_t sB,
-    int64_t K, int tilesN, int upper, int per, int base, int split, Epi epi) {
+    int64_t K, int tilesN, int upper, int per, int base, int split, int nwork, Epi epi) {
   using G = GemmGeom<TILE>;
   constexpr int NA = (PR & kLH) ? 2 : 1;        // A planes
   constexpr int NB = (PR & kHL) ? 2 : 1;        // B planes
@@ -800,12 +800,18 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
   constexpr int LP = PLANE / G::NT;             // loads per thread per plane
   constexpr int KS = BK / 16;
   __shared__ u16x8 lds[2][NPL][PLANE];          // [stage][Ah, (Al), Bh, (Bl)]
+  // Work items w = blockIdx.x, blockIdx.x + gridDim.x, ... < nwork: a full
+  // grid stays resident (one round of workgroups) and each workgroup takes
+  // its next tile after its epilogue, so the rounds of the CUs drift apart
+  // instead of each waiting for the slowest CU (the mixed 32-layer set
+  // 601 -> 592 ms, same box).  A split launch has one item per workgroup.
+  for (int w = int(blockIdx.x); w < nwork; w += int(gridDim.x)) {
   // Work item f = matrix * per + tile, in units of the tiles that tilesN
   // counts, tiles in the grouped order (which only decides which workgroup
   // computes a tile, never how).  With split, each such tile (twice TILE on a
   // side) is done by four workgroups, one per TILE-quarter; a symmetric
   // output skips the quarter below the diagonal.
-  const int f = base + (split ? int(blockIdx.x >> 2) : xcd_item(int(blockIdx.x), int(gridDim.x)));
+  const int f = base + (split ? (w >> 2) : xcd_item(w, nwork));
   const int z = __builtin_amdgcn_readfirstlane(f / per);
   int ti, tj;
   if (upper) grouped_upper_coords(f - z * per, tilesN, ti, tj);
@@ -814,10 +820,14 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
     const int q = int(blockIdx.x & 3);
     ti = 2 * ti + (q >> 1);
     tj = 2 * tj + (q & 1);
-    if (upper && ti > tj) return;
+    if (upper && ti > tj) continue;
   }
   const int64_t row0 = int64_t(ti) * TILE, col0 = int64_t(tj) * TILE;
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  // the thread's lane terms are recomputed per tile (an opaque copy of the
+  // thread index), so no per-lane value is held across the epilogue
+  int t = int(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  const int lane = t & 63, wv = t >> 6;
   const int wr = (wv / G::WN) * G::TMW, wc = (wv % G::WN) * G::TNW;
 
   const uint16_t* gsrc[NPL];
@@ -966,6 +976,8 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
       epi.col(un, z, tj0 + er, ti0 + ec, v, diag, in[u & 1]);
     }
   }
+  __syncthreads();  // the staging slots overlap the next tile's first stage
+  }
 }
 
 // ============================================================================
@@ -1040,11 +1052,12 @@ __global__ __launch_bounds__(256) void ns0_kernel(MatTable tab, StepScalars sc, 
 static hipError_t last_launch() { return hipGetLastError(); }
 
 // One batched bf16 GEMM launch over `per` tiles of each of `count` matrices.
-// A grid runs in rounds of PER_CU workgroups per CU.  When the last round is
-// partial, its tiles run in a second launch at half the tile size, four
-// workgroups per tile (three on the diagonal of a symmetric output), so that
-// round costs a fraction of a full one on an otherwise idle chip.  Tile size
-// changes no bit of the result.
+// A grid runs in rounds of PER_CU workgroups per CU: the main launch is one
+// resident round of workgroups that take the full rounds' tiles in turn.
+// When the last round is partial, its tiles run in a second launch at half
+// the tile size, four workgroups per tile (three on the diagonal of a
+// symmetric output), so that round costs a fraction of a full one on an
+// otherwise idle chip.  Tile size changes no bit of the result.
 template <int TILE, int PR, typename Epi>
 static hipError_t gemm_launch(const uint16_t* Ah, const uint16_t* Al, int64_t lda, int64_t sA, const uint16_t* Bh,
                               const uint16_t* Bl, int64_t ldb, int64_t sB, int64_t K, int tilesN, int upper, int per,
@@ -1053,14 +1066,15 @@ static hipError_t gemm_launch(const uint16_t* Ah, const uint16_t* Al, int64_t ld
   const int total = per * count;
   const int round = cus * GemmGeom<TILE>::PER_CU;
   const int main = (cus > 0 && total > round) ? total - total % round : total;
-  hipLaunchKernelGGL((gemm_bf16_kernel<TILE, PR, Epi>), dim3(unsigned(main)), dim3(GemmGeom<TILE>::NT), 0, st,
-                     Ah, Al, lda, sA, Bh, Bl, ldb, sB, K, tilesN, upper, per, 0, 0, epi);
+  const int grid = (cus > 0 && main > round) ? round : main;
+  hipLaunchKernelGGL((gemm_bf16_kernel<TILE, PR, Epi>), dim3(unsigned(grid)), dim3(GemmGeom<TILE>::NT), 0, st,
+                     Ah, Al, lda, sA, Bh, Bl, ldb, sB, K, tilesN, upper, per, 0, 0, main, epi);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (main == total) return hipSuccess;
   constexpr int SUB = TILE / 2;
   hipLaunchKernelGGL((gemm_bf16_kernel<SUB, PR, Epi>), dim3(unsigned(4 * (total - main))),
                      dim3(GemmGeom<SUB>::NT), 0, st, Ah, Al, lda, sA, Bh, Bl, ldb, sB, K, tilesN, upper, per, main, 1,
-                     epi);
+                     4 * (total - main), epi);
   return hipGetLastError();
 }
 

@@ -41,8 +41,8 @@ TRAFFIC = {
            "fetch_kib_per_dispatch": 83727.4, "write_kib_per_dispatch": 109375.8,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
-           "kernel_source_sha256": "034d7c2e6f94f2fecef5806da0850929b59f8c363d3531812e6543d4083d47cc",
-           "fetch_kib_per_dispatch": 11983334.3, "write_kib_per_dispatch": 1548857.5,
+           "kernel_source_sha256": "7967fbf1368cbcf17533fe19d7459d34e0883de5c215939d90aea5e9a3882cad",
+           "fetch_kib_per_dispatch": 12438558.8, "write_kib_per_dispatch": 1640442.6,
            "fetch_scale": 2.0, "write_scale": 1.0},
 }
 

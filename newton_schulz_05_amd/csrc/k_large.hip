@@ -27,6 +27,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace muon {
 
 // ============================================================================
@@ -212,13 +214,19 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ nor
 // Epilogues.
 //
 // bf16 MFMA path: the GEMM stages each 32 x 32 MFMA tile of the output
-// through LDS and hands the epilogue
-//   row(z, i, j0, v[16], diag): C[i][j0 .. j0+15], which it may replace by
+// through LDS and hands the epilogue runs of kRun = 8 consecutive elements,
+// four lanes to a 32-element row of the tile and 16 rows per wave
+// instruction:
+//   row(z, i, j0, v[8], diag): C[i][j0 .. j0+7], which it may replace by
 //       the final values (the column pass sees them), and
-//   col(z, j, i0, v[16], diag): the final values C[i0 .. i0+15][j], for the
-//       mirrored (symmetric outputs) or transposed (X^T, tall W) stores,
-// so that every store is a run of 16 consecutive elements (16-byte vectors
-// where aligned).  `diag` is true on tiles on the diagonal of a symmetric
+//   col(z, j, i0, v[8], diag): the final values C[i0 .. i0+7][j], for the
+//       mirrored (symmetric outputs) or transposed (X^T, tall W) stores.
+// So a bf16 store instruction writes 64 contiguous bytes of each of 16 rows.
+// Measured on this GPU with a few workgroups writing 256 x 256 tiles (so
+// that no shared bandwidth limits them), a CU stores 100-110 GB/s in that
+// pattern against 58-65 GB/s with two lanes to a row (16 elements a lane,
+// two 16-byte pieces 32 bytes apart per instruction), and fp32 runs of 16
+// written that way only 31-35 GB/s.  `diag` is true on tiles on the diagonal of a symmetric
 // output, where only i <= j is owned by the row pass and i < j is mirrored.
 // Memory reads happen outside row() and col(), so that no read waits behind
 // the stores of an earlier sub-tile (the vector memory counter retires loads
@@ -236,15 +244,18 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* __restrict__ nor
 // column j.
 // ============================================================================
 
-// 16 consecutive elements; elements [k0, k1) are loaded / stored (the
+// elements per epilogue run
+constexpr int kRun = 8;
+
+// kRun consecutive elements; elements [k0, k1) are loaded / stored (the
 // others of v are left alone), with 16-byte vectors when the run is whole
 // and aligned.
 template <typename T> struct Seg;
 template <> struct Seg<float> {
   __device__ static __forceinline__ void load(const float* p, int k0, int k1, float* v) {
-    if (k0 == 0 && k1 == 16 && ((uintptr_t)p & 15) == 0) {
+    if (k0 == 0 && k1 == kRun && ((uintptr_t)p & 15) == 0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < kRun / 4; ++q) {
         const f32x4 x = ((const f32x4*)p)[q];
         v[4 * q] = x[0]; v[4 * q + 1] = x[1]; v[4 * q + 2] = x[2]; v[4 * q + 3] = x[3];
       }
@@ -253,9 +264,9 @@ template <> struct Seg<float> {
     for (int k = k0; k < k1; ++k) v[k] = p[k];
   }
   __device__ static __forceinline__ void store(float* p, int k0, int k1, const float* v) {
-    if (k0 == 0 && k1 == 16 && ((uintptr_t)p & 15) == 0) {
+    if (k0 == 0 && k1 == kRun && ((uintptr_t)p & 15) == 0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ((f32x4*)p)[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+      for (int q = 0; q < kRun / 4; ++q) ((f32x4*)p)[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
       return;
     }
     for (int k = k0; k < k1; ++k) p[k] = v[k];
@@ -263,9 +274,9 @@ template <> struct Seg<float> {
 };
 template <> struct Seg<uint16_t> {
   __device__ static __forceinline__ void load(const uint16_t* p, int k0, int k1, float* v) {
-    if (k0 == 0 && k1 == 16 && ((uintptr_t)p & 15) == 0) {
+    if (k0 == 0 && k1 == kRun && ((uintptr_t)p & 15) == 0) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < kRun / 8; ++q) {
         const u32x4 x = ((const u32x4*)p)[q];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -278,9 +289,9 @@ template <> struct Seg<uint16_t> {
     for (int k = k0; k < k1; ++k) v[k] = bf2f(p[k]);
   }
   __device__ static __forceinline__ void store(uint16_t* p, int k0, int k1, const float* v) {
-    if (k0 == 0 && k1 == 16 && ((uintptr_t)p & 15) == 0) {
+    if (k0 == 0 && k1 == kRun && ((uintptr_t)p & 15) == 0) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int q = 0; q < kRun / 8; ++q)
         ((u32x4*)p)[q] = u32x4{f2bf2(v[8 * q], v[8 * q + 1]), f2bf2(v[8 * q + 2], v[8 * q + 3]),
                                f2bf2(v[8 * q + 4], v[8 * q + 5]), f2bf2(v[8 * q + 6], v[8 * q + 7])};
       return;
@@ -289,26 +300,26 @@ template <> struct Seg<uint16_t> {
   }
 };
 
-__device__ __forceinline__ int clamp16(int64_t x) { return x <= 0 ? 0 : (x >= 16 ? 16 : int(x)); }
+__device__ __forceinline__ int clamp_run(int64_t x) { return x <= 0 ? 0 : (x >= kRun ? kRun : int(x)); }
 
-// 16 consecutive elements held as loaded (16-byte vectors, not yet
+// kRun consecutive elements held as loaded (16-byte vectors, not yet
 // converted), so that an epilogue issues the loads of a sub-tile before the
 // stores of the previous one and waits for them only where it uses them.
 // The address must be 16-byte aligned.
 template <typename T> struct Run;
 template <> struct Run<float> {
-  f32x4 q[4];
+  f32x4 q[kRun / 4];
   __device__ __forceinline__ void fetch(const float* p) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) q[k] = ((const f32x4*)p)[k];
+    for (int k = 0; k < kRun / 4; ++k) q[k] = ((const f32x4*)p)[k];
   }
   __device__ __forceinline__ float operator[](int k) const { return q[k >> 2][k & 3]; }
 };
 template <> struct Run<uint16_t> {
-  u32x4 q[2];
+  u32x4 q[kRun / 8];
   __device__ __forceinline__ void fetch(const uint16_t* p) {
-    q[0] = ((const u32x4*)p)[0];
-    q[1] = ((const u32x4*)p)[1];
+#pragma unroll
+    for (int k = 0; k < kRun / 8; ++k) q[k] = ((const u32x4*)p)[k];
   }
   __device__ __forceinline__ float operator[](int k) const {
     const uint32_t w = q[k >> 3][(k >> 1) & 3];
@@ -333,7 +344,7 @@ struct NatStore {
     }
   }
   // the same for `cnt` consecutive stored elements starting at idx0; `pre`,
-  // when given, holds the 16 W values already loaded (cnt == 16)
+  // when given, holds the kRun W values already loaded (cnt == kRun)
   template <typename PT>
   __device__ static __forceinline__ void put_seg(const MatRef& r, const StepScalars& sc, int64_t idx0, int cnt,
                                                  const float* o, const Run<PT>* pre = nullptr) {
@@ -343,16 +354,16 @@ struct NatStore {
       return;
     }
     PT* W = (PT*)r.w + idx0;
-    float w[16] = {};
+    float w[kRun] = {};
     if (pre) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) w[k] = (*pre)[k];
+      for (int k = 0; k < kRun; ++k) w[k] = (*pre)[k];
     } else {
       Seg<PT>::load(W, 0, cnt, w);
     }
     const float keep = 1.0f - sc.lr * sc.wd;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) w[k] = fmaf(-sc.lr * sc.scale, o[k], w[k] * keep);
+    for (int k = 0; k < kRun; ++k) w[k] = fmaf(-sc.lr * sc.scale, o[k], w[k] * keep);
     Seg<PT>::store(W, 0, cnt, w);
   }
 };
@@ -371,24 +382,24 @@ struct EpiGramBf16 {
   __device__ __forceinline__ void row(const Uni& un, int z, int64_t i, int64_t j0, float* v, bool diag,
                                       const In&) const {
     const float s2 = un.s2;
-    float lo[16];
+    float lo[kRun];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < kRun; ++k) {
       v[k] *= s2;
       lo[k] = v[k] - bf2f(f2bf(v[k]));
     }
-    const int k0 = diag ? clamp16(i - j0) : 0;  // diagonal tiles: j >= i
+    const int k0 = diag ? clamp_run(i - j0) : 0;  // diagonal tiles: j >= i
     const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
-    Seg<float>::store(A + o, k0, 16, v);
-    Seg<uint16_t>::store(H + o, k0, 16, v);
-    if (with_lo) Seg<uint16_t>::store(L + o, k0, 16, lo);
+    Seg<float>::store(A + o, k0, kRun, v);
+    Seg<uint16_t>::store(H + o, k0, kRun, v);
+    if (with_lo) Seg<uint16_t>::store(L + o, k0, kRun, lo);
   }
   __device__ __forceinline__ void col(const Uni&, int z, int64_t j, int64_t i0, const float* v, bool diag,
                                       const In&) const {
-    float lo[16];
+    float lo[kRun];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
-    const int k1 = diag ? clamp16(j - i0) : 16;  // diagonal tiles: mirror i < j only
+    for (int k = 0; k < kRun; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
+    const int k1 = diag ? clamp_run(j - i0) : kRun;  // diagonal tiles: mirror i < j only
     const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
     Seg<uint16_t>::store(H + o, 0, k1, v);
     if (with_lo) Seg<uint16_t>::store(L + o, 0, k1, lo);
@@ -410,11 +421,11 @@ struct EpiPolyBf16 {
   __device__ __forceinline__ void row(const Uni& un, int z, int64_t i, int64_t j0, float* v, bool diag,
                                       const In& in) const {
     const float ps = un.ps;
-    const int k0 = diag ? clamp16(i - j0) : 0;
+    const int k0 = diag ? clamp_run(i - j0) : 0;
     const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
-    float pv[16];
+    float pv[kRun];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < kRun; ++k) {
       float p = fmaf(c, v[k], b * in.a[k]);
       if (i == j0 + k) {
         p = ps * (p + a);
@@ -426,23 +437,23 @@ struct EpiPolyBf16 {
       }
       v[k] = p;
     }
-    Seg<uint16_t>::store(Poff + o, k0, 16, pv);
+    Seg<uint16_t>::store(Poff + o, k0, kRun, pv);
     if (PoffL) {
-      float lo[16];
+      float lo[kRun];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) lo[k] = pv[k] - bf2f(f2bf(pv[k]));
-      Seg<uint16_t>::store(PoffL + o, k0, 16, lo);
+      for (int k = 0; k < kRun; ++k) lo[k] = pv[k] - bf2f(f2bf(pv[k]));
+      Seg<uint16_t>::store(PoffL + o, k0, kRun, lo);
     }
   }
   __device__ __forceinline__ void col(const Uni&, int z, int64_t j, int64_t i0, const float* v, bool diag,
                                       const In&) const {
-    const int k1 = diag ? clamp16(j - i0) : 16;
+    const int k1 = diag ? clamp_run(j - i0) : kRun;
     const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
     Seg<uint16_t>::store(Poff + o, 0, k1, v);
     if (PoffL) {
-      float lo[16];
+      float lo[kRun];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
+      for (int k = 0; k < kRun; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
       Seg<uint16_t>::store(PoffL + o, 0, k1, lo);
     }
   }
@@ -466,27 +477,27 @@ struct EpiSymMul {
   }
   __device__ __forceinline__ void row(const Uni&, int z, int64_t i, int64_t j0, float* v, bool diag,
                                       const In& in) const {
-    const int k0 = diag ? clamp16(i - j0) : 0;  // diagonal tiles: j >= i
+    const int k0 = diag ? clamp_run(i - j0) : 0;  // diagonal tiles: j >= i
     const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
-    float lo[16];
+    float lo[kRun];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < kRun; ++k) {
       v[k] = fmaf(in.d, in.s[k], v[k]);
       lo[k] = v[k] - bf2f(f2bf(v[k]));
     }
-    Seg<float>::store(S + o, k0, 16, v);
-    Seg<uint16_t>::store(H + o, k0, 16, v);
-    if (with_lo) Seg<uint16_t>::store(L + o, k0, 16, lo);
+    Seg<float>::store(S + o, k0, kRun, v);
+    Seg<uint16_t>::store(H + o, k0, kRun, v);
+    if (with_lo) Seg<uint16_t>::store(L + o, k0, kRun, lo);
   }
   __device__ __forceinline__ void col(const Uni&, int z, int64_t j, int64_t i0, const float* v, bool diag,
                                       const In&) const {
-    const int k1 = diag ? clamp16(j - i0) : 16;  // diagonal tiles: mirror i < j only
+    const int k1 = diag ? clamp_run(j - i0) : kRun;  // diagonal tiles: mirror i < j only
     const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
     Seg<uint16_t>::store(H + o, 0, k1, v);
     if (with_lo) {
-      float lo[16];
+      float lo[kRun];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
+      for (int k = 0; k < kRun; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
       Seg<uint16_t>::store(L + o, 0, k1, lo);
     }
   }
@@ -498,7 +509,9 @@ struct EpiSymMul {
 // acc = Poff1 Poff0^T from the GEMM, plus Pd1[i] Poff0[i][j] +
 // Poff1[i][j] Pd0[j] + [i == j] Pd1[i] Pd0[i].  Off-diagonal R in bf16
 // (mirrored; its lo part in RoffL when given), diagonal in fp32, the layout
-// the apply and the next R take.
+// the apply and the next R take.  Lo: the factors may carry lo planes (the
+// precise recipe), which the lean recipe's epilogue holds no registers for.
+template <bool Lo>
 struct EpiPairR {
   const uint16_t* Poff0; const uint16_t* Poff0L; const float* Pd0;
   const uint16_t* Poff1; const uint16_t* Poff1L; const float* Pd1;
@@ -508,28 +521,35 @@ struct EpiPairR {
   // they are fetched just before their sub-tile
   static constexpr bool kAhead = false;
   struct Uni { float ps; };
-  struct In { Run<uint16_t> p0, p1, p0l, p1l; Run<float> d0; float d1; };
+  struct InH { Run<uint16_t> p0, p1; Run<float> d0; float d1; };
+  struct InL : InH { Run<uint16_t> p0l, p1l; };
+  using In = std::conditional_t<Lo, InL, InH>;
   __device__ __forceinline__ Uni uni(int z) const { return Uni{use_scale ? scal[z * 4 + 0] : 1.0f}; }
   __device__ __forceinline__ void fetch(const Uni&, int z, int64_t i, int64_t j0, int64_t, int64_t, In& in) const {
     const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
     in.p0.fetch(Poff0 + o);
     in.p1.fetch(Poff1 + o);
-    if (Poff0L) in.p0l.fetch(Poff0L + o);
-    if (Poff1L) in.p1l.fetch(Poff1L + o);
+    if constexpr (Lo) {
+      if (Poff0L) in.p0l.fetch(Poff0L + o);
+      if (Poff1L) in.p1l.fetch(Poff1L + o);
+    }
     in.d0.fetch(Pd0 + int64_t(z) * mp + j0);
     in.d1 = Pd1[int64_t(z) * mp + i];
   }
   __device__ __forceinline__ void row(const Uni& un, int z, int64_t i, int64_t j0, float* v, bool diag,
                                       const In& in) const {
     const float ps = un.ps;
-    const int k0 = diag ? clamp16(i - j0) : 0;
+    const int k0 = diag ? clamp_run(i - j0) : 0;
     const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
-    float rv[16];
+    float rv[kRun];
     const float d1 = in.d1;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float p0 = Poff0L ? in.p0[k] + in.p0l[k] : in.p0[k];
-      const float p1 = Poff1L ? in.p1[k] + in.p1l[k] : in.p1[k];
+    for (int k = 0; k < kRun; ++k) {
+      float p0 = in.p0[k], p1 = in.p1[k];
+      if constexpr (Lo) {
+        if (Poff0L) p0 += in.p0l[k];
+        if (Poff1L) p1 += in.p1l[k];
+      }
       const float d0 = in.d0[k];
       float r = fmaf(d1, p0, fmaf(p1, d0, v[k]));
       if (i == j0 + k) {
@@ -542,42 +562,44 @@ struct EpiPairR {
       }
       v[k] = r;
     }
-    Seg<uint16_t>::store(Roff + o, k0, 16, rv);
+    Seg<uint16_t>::store(Roff + o, k0, kRun, rv);
     if (RoffL) {
-      float lo[16];
+      float lo[kRun];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) lo[k] = rv[k] - bf2f(f2bf(rv[k]));
-      Seg<uint16_t>::store(RoffL + o, k0, 16, lo);
+      for (int k = 0; k < kRun; ++k) lo[k] = rv[k] - bf2f(f2bf(rv[k]));
+      Seg<uint16_t>::store(RoffL + o, k0, kRun, lo);
     }
   }
   __device__ __forceinline__ void col(const Uni&, int z, int64_t j, int64_t i0, const float* v, bool diag,
                                       const In&) const {
-    const int k1 = diag ? clamp16(j - i0) : 16;
+    const int k1 = diag ? clamp_run(j - i0) : kRun;
     const int64_t o = int64_t(z) * mp * mp + j * mp + i0;
     Seg<uint16_t>::store(Roff + o, 0, k1, v);
     if (RoffL) {
-      float lo[16];
+      float lo[kRun];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
+      for (int k = 0; k < kRun; ++k) lo[k] = v[k] - bf2f(f2bf(v[k]));
       Seg<uint16_t>::store(RoffL + o, 0, k1, lo);
     }
   }
 };
 
 // Apply (bf16 path): X' = acc + Pd[i] * X[i][j] (X = hi + lo when Xl is
-// given); X' and X'^T in bf16, or on the last step the weight update (O) at
-// the stored position
-template <typename PT>
+// given); X' and X'^T in bf16, or on the last step (Last) the weight update
+// (O) at the stored position
+template <typename PT, bool Last>
 struct EpiApplyBf16 {
   MatTable tab; StepScalars sc; uint16_t* X; const uint16_t* Xl; uint16_t* XtN; const float* Pd;
-  int64_t mp, np, m, n; int last;
+  int64_t mp, np, m, n;
   static constexpr bool kCol = true;
-  // the matrix's stored orientation and W; per sub-tile X's run (hi and lo
+  // the matrix's stored orientation and W; per run X's run (hi and lo
   // planes), Pd[i], and on the last step the W run the update reads (the row
   // run for a member stored as is, the column run for a transposed one) when
   // it is whole and 16-byte aligned (otherwise the update loads W itself)
   struct Uni { MatRef e; int tr; };
-  struct In { Run<uint16_t> x, xl; float d; Run<PT> w; int64_t widx; int wcnt; bool wpre; };
+  struct InX { Run<uint16_t> x, xl; float d; };
+  struct InW : InX { Run<PT> w; int64_t widx; int wcnt; bool wpre; };
+  using In = std::conditional_t<Last, InW, InX>;
   __device__ __forceinline__ Uni uni(int z) const { return Uni{tab.e[z], tab.tr[z] != 0}; }
   __device__ __forceinline__ void fetch(const Uni& un, int z, int64_t i, int64_t j0, int64_t jc, int64_t ic,
                                         In& in) const {
@@ -585,36 +607,35 @@ struct EpiApplyBf16 {
     in.x.fetch(X + o);
     if (Xl) in.xl.fetch(Xl + o);
     in.d = Pd[int64_t(z) * mp + i];
-    in.wpre = false;
-    if (last) {
+    if constexpr (Last) {
       if (!un.tr) {
         in.widx = i * n + j0;
-        in.wcnt = (i < m) ? clamp16(n - j0) : 0;
+        in.wcnt = (i < m) ? clamp_run(n - j0) : 0;
       } else {
         in.widx = jc * m + ic;
-        in.wcnt = (jc < n) ? clamp16(m - ic) : 0;
+        in.wcnt = (jc < n) ? clamp_run(m - ic) : 0;
       }
       const PT* W = (const PT*)un.e.w + in.widx;
-      in.wpre = sc.mode != 1 && in.wcnt == 16 && ((uintptr_t)W & 15) == 0;
+      in.wpre = sc.mode != 1 && in.wcnt == kRun && ((uintptr_t)W & 15) == 0;
       if (in.wpre) in.w.fetch(W);
     }
   }
   __device__ __forceinline__ void row(const Uni& un, int z, int64_t i, int64_t j0, float* v, bool,
                                       const In& in) const {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = fmaf(in.d, Xl ? in.x[k] + in.xl[k] : in.x[k], v[k]);
-    if (!last) {
-      Seg<uint16_t>::store(X + int64_t(z) * mp * np + i * np + j0, 0, 16, v);
-    } else if (!un.tr) {
-      NatStore::put_seg<PT>(un.e, sc, in.widx, in.wcnt, v, in.wpre ? &in.w : nullptr);
+    for (int k = 0; k < kRun; ++k) v[k] = fmaf(in.d, Xl ? in.x[k] + in.xl[k] : in.x[k], v[k]);
+    if constexpr (!Last) {
+      Seg<uint16_t>::store(X + int64_t(z) * mp * np + i * np + j0, 0, kRun, v);
+    } else {
+      if (!un.tr) NatStore::put_seg<PT>(un.e, sc, in.widx, in.wcnt, v, in.wpre ? &in.w : nullptr);
     }
   }
   __device__ __forceinline__ void col(const Uni& un, int z, int64_t j, int64_t i0, const float* v, bool,
                                       const In& in) const {
-    if (!last) {
-      Seg<uint16_t>::store(XtN + int64_t(z) * mp * np + j * mp + i0, 0, 16, v);
-    } else if (un.tr) {
-      NatStore::put_seg<PT>(un.e, sc, in.widx, in.wcnt, v, in.wpre ? &in.w : nullptr);
+    if constexpr (!Last) {
+      Seg<uint16_t>::store(XtN + int64_t(z) * mp * np + j * mp + i0, 0, kRun, v);
+    } else {
+      if (un.tr) NatStore::put_seg<PT>(un.e, sc, in.widx, in.wcnt, v, in.wpre ? &in.w : nullptr);
     }
   }
 };
@@ -757,7 +778,8 @@ __device__ __forceinline__ void grouped_upper_coords(int t, int T, int& ti, int&
 constexpr int kHH = 1, kHL = 2, kLH = 4;
 
 // whether an epilogue's inputs are fetched one sub-tile ahead (the default)
-// or just before their sub-tile (Epi::kAhead = false)
+// or just before their run (Epi::kAhead = false: inputs used by the row
+// pass only)
 template <typename Epi, typename = void> struct EpiAhead { static constexpr bool value = true; };
 template <typename Epi> struct EpiAhead<Epi, decltype(void(Epi::kAhead))> { static constexpr bool value = Epi::kAhead; };
 
@@ -895,85 +917,118 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
       }
     }
   };
-  auto compute = [&](int st) {
+  auto mfma_slice = [&](int q) {
+#pragma unroll
+    for (int a = 0; a < G::FM; ++a)
+#pragma unroll
+      for (int b = 0; b < G::FN; ++b) {
+        acc[a][b] = mfma32x32x16(fa[q][0][a], fb[q][0][b], acc[a][b]);
+        if constexpr ((PR & kHL) != 0) acc[a][b] = mfma32x32x16(fa[q][0][a], fb[q][NB - 1][b], acc[a][b]);
+        if constexpr ((PR & kLH) != 0) acc[a][b] = mfma32x32x16(fa[q][NA - 1][a], fb[q][0][b], acc[a][b]);
+      }
+  };
+  // a k-tile in stage st: all its fragment reads and the MFMAs of all but
+  // its last k slice (head), then the last slice from registers (tail)
+  auto head = [&](int st) {
     lread(st, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) lread(st, ks + 1, (ks + 1) & 1);
-      const int q = ks & 1;
-#pragma unroll
-      for (int a = 0; a < G::FM; ++a)
-#pragma unroll
-        for (int b = 0; b < G::FN; ++b) {
-          acc[a][b] = mfma32x32x16(fa[q][0][a], fb[q][0][b], acc[a][b]);
-          if constexpr ((PR & kHL) != 0) acc[a][b] = mfma32x32x16(fa[q][0][a], fb[q][NB - 1][b], acc[a][b]);
-          if constexpr ((PR & kLH) != 0) acc[a][b] = mfma32x32x16(fa[q][NA - 1][a], fb[q][0][b], acc[a][b]);
-        }
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      lread(st, ks + 1, (ks + 1) & 1);
+      mfma_slice(ks & 1);
     }
   };
+  auto tail = [&]() { mfma_slice((KS - 1) & 1); };
+  // stage st's loads have landed and every wave has read the other stage
+  auto stage_sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // two stages: the loads of k-tile k+1 fly while k-tile k is multiplied;
-  // stage u^1 was last read before the barrier that ended the previous tile.
-  // KT is even (K is a multiple of 128), so the loop body is straight-line
-  // code over a pair of k-tiles; the last pair's second load fetches the
-  // last k-tile again into the free stage (never read; the barrier before the
-  // epilogue waits for it).
+  // Two stages: the loads of k-tile t+1 fly while k-tile t is multiplied.
+  // Each k-tile's last slice is multiplied after the barrier that frees its
+  // stage, once the next loads into that stage are issued, so the waves
+  // have MFMAs to issue while those loads start (the order of the products
+  // into each accumulator is unchanged).  The scheduling barriers fix this
+  // order: left to itself the compiler moved a varying share of a stage's
+  // MFMAs below the wait, up to all of them in one build of the three-plane
+  // apply (10% slower).  KT is even (K is a multiple of 128): the loop body
+  // is straight-line code over a pair of k-tiles, the last pair peeled.
   const int KT = int(K / BK);
   gload(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int kt = 0; kt < KT; kt += 2) {
-    gload(int64_t(kt + 1) * BK, 1);
-    compute(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int kn = (kt + 2 < KT) ? kt + 2 : KT - 1;
-    gload(int64_t(kn) * BK, 0);
-    compute(1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  gload(BK, 1);
+  head(0);
+  for (int kt = 0; kt + 2 < KT; kt += 2) {
+    stage_sync();                     // k-tile kt + 1 in stage 1
+    gload(int64_t(kt + 2) * BK, 0);
+    tail();                           // k-tile kt
+    head(1);                          // k-tile kt + 1
+    stage_sync();                     // k-tile kt + 2 in stage 0
+    gload(int64_t(kt + 3) * BK, 1);
+    tail();                           // k-tile kt + 1
+    head(0);                          // k-tile kt + 2
   }
+  stage_sync();                       // k-tile KT - 1 in stage 1
+  tail();                             // k-tile KT - 2
+  head(1);                            // k-tile KT - 1
+  tail();
 
   // Epilogue: each wave stages one 32 x 32 MFMA tile at a time in its own LDS
-  // slot (the operand stages are free now) and reads it back as row runs
-  // (lane l: row l/2, columns 16 (l%2) ..) and column runs.
+  // slot (the operand stages are free now) and reads it back as row runs and
+  // column runs of kRun elements: lane l takes rows (l / 4) and (l / 4) + 16,
+  // columns kRun (l % 4) .. (the column pass the same with rows and columns
+  // exchanged).
   __syncthreads();
   constexpr int kLd = 36;  // slot row stride in floats
+  constexpr int kLpr = 32 / kRun;        // lanes per row of the sub-tile
+  constexpr int kRH = 64 / kLpr;         // rows per wave instruction (16)
   float* slot = reinterpret_cast<float*>(&lds[0][0][0]) + wv * (32 * kLd);
   const bool diag = upper && (ti == tj);
-  const int er = lane >> 1, ec = (lane & 1) * 16;
+  const int er = lane / kLpr, ec = (lane % kLpr) * kRun;
   // the matrix's values once, then the wave's MFMA tiles in order, each
-  // one's inputs fetched one tile ahead
+  // one's inputs (two runs a lane) fetched one tile ahead
   const typename Epi::Uni un = epi.uni(z);
   constexpr int NTL = G::FM * G::FN;
-  typename Epi::In in[2];
-  auto fetch = [&](int u, typename Epi::In& dst) {
+  typename Epi::In in[2][2];
+  auto fetch = [&](int u, typename Epi::In* dst) {
     const int64_t ti0 = row0 + wr + (u / G::FN) * 32, tj0 = col0 + wc + (u % G::FN) * 32;
-    epi.fetch(un, z, ti0 + er, tj0 + ec, tj0 + er, ti0 + ec, dst);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      epi.fetch(un, z, ti0 + er + h * kRH, tj0 + ec, tj0 + er + h * kRH, ti0 + ec, dst[h]);
   };
   constexpr bool ahead = EpiAhead<Epi>::value;
   if (ahead) fetch(0, in[0]);
 #pragma unroll
   for (int u = 0; u < NTL; ++u) {
-    if (ahead) {
-      if (u + 1 < NTL) fetch(u + 1, in[(u + 1) & 1]);
-    } else {
-      fetch(u, in[u & 1]);
-    }
+    if (ahead && u + 1 < NTL) fetch(u + 1, in[(u + 1) & 1]);
     const int a = u / G::FN, b = u % G::FN;
     const int64_t ti0 = row0 + wr + a * 32, tj0 = col0 + wc + b * 32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) slot[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kLd + (lane & 31)] = acc[a][b][r];
-    float v[16];
+    float v[2][kRun];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = slot[er * kLd + ec + k];
-    epi.row(un, z, ti0 + er, tj0 + ec, v, diag, in[u & 1]);
+    for (int h = 0; h < 2; ++h) {
+      // inputs fetched just before their run (the row pass is their only user)
+      if (!ahead) epi.fetch(un, z, ti0 + er + h * kRH, tj0 + ec, tj0 + er + h * kRH, ti0 + ec, in[u & 1][h]);
+#pragma unroll
+      for (int k = 0; k < kRun; ++k) v[h][k] = slot[(er + h * kRH) * kLd + ec + k];
+      epi.row(un, z, ti0 + er + h * kRH, tj0 + ec, v[h], diag, in[u & 1][h]);
+    }
     if constexpr (Epi::kCol) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) slot[er * kLd + ec + k] = v[k];
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = slot[(ec + k) * kLd + er];
-      epi.col(un, z, tj0 + er, ti0 + ec, v, diag, in[u & 1]);
+        for (int k = 0; k < kRun; ++k) slot[(er + h * kRH) * kLd + ec + k] = v[h][k];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) v[h][k] = slot[(ec + k) * kLd + er + h * kRH];
+        epi.col(un, z, tj0 + er + h * kRH, ti0 + ec, v[h], diag, in[u & 1][h]);
+      }
     }
   }
   __syncthreads();  // the staging slots overlap the next tile's first stage
@@ -1192,35 +1247,46 @@ static hipError_t ns_group_bf16(const LargeArgs& g, hipStream_t st, int k, int G
     const uint16_t* r0 = (j == 1) ? Pb[0] : Rb[(j - 1) & 1];
     const uint16_t* r0l = (j == 1) ? PbL[0] : RbL[(j - 1) & 1];
     const float* rd0 = (j == 1) ? Pdb[0] : Rdb[(j - 1) & 1];
-    EpiPairR er{r0, cs ? r0l : nullptr, rd0, Pb[j & 1], cs ? PbL[j & 1] : nullptr, Pdb[j & 1],
-                Rb[j & 1], cs ? RbL[j & 1] : nullptr, Rdb[j & 1], scal, (k == 0 && j == 1) ? 1 : 0, mp};
     const bool r3 = cs && !(g.m >= kRSingleFromM && steps <= kLeanMaxSteps);
-    if ((e = r3 ? sym3(Pb[j & 1], PbL[j & 1], r0, r0l, er) : sym1(Pb[j & 1], r0, er)) != hipSuccess) return e;
+    if (cs) {
+      EpiPairR<true> er{r0, r0l, rd0, Pb[j & 1], PbL[j & 1], Pdb[j & 1], Rb[j & 1], RbL[j & 1], Rdb[j & 1], scal,
+                        (k == 0 && j == 1) ? 1 : 0, mp};
+      e = r3 ? sym3(Pb[j & 1], PbL[j & 1], r0, r0l, er) : sym1(Pb[j & 1], r0, er);
+    } else {
+      EpiPairR<false> er{r0, nullptr, rd0, Pb[j & 1], nullptr, Pdb[j & 1], Rb[j & 1], nullptr, Rdb[j & 1], scal,
+                         (k == 0 && j == 1) ? 1 : 0, mp};
+      e = sym1(Pb[j & 1], r0, er);
+    }
+    if (e != hipSuccess) return e;
   }
   // apply with R (P_0 for a single step): A = R (+ its lo plane, precise),
   // B = Xt (+ X_0's lo plane)
   const uint16_t* ra = (G == 1) ? Pb[0] : Rb[(G - 1) & 1];
   const uint16_t* ral = (G == 1) ? PbL[0] : RbL[(G - 1) & 1];
   const float* rd = (G == 1) ? Pdb[0] : Rdb[(G - 1) & 1];
-  EpiApplyBf16<PT> eap{g.tab, g.sc, X, xlo ? Xl : nullptr, Xt[cur ^ 1], rd, mp, np, g.m, g.n, last};
   const uint16_t* bl = xlo ? Xtl : nullptr;
   // algorithmic work of this apply (one m x m by m x n product per matrix)
   // and the MFMA work it executes (one such product per operand-plane pair)
   const double alg = 2.0 * double(g.m) * double(g.m) * double(g.n) * g.count;
   const int prods = 1 + (xlo ? 1 : 0) + (cs ? 1 : 0);
+  auto apply = [&](const auto& eap) {
+    if (cs && xlo)
+      return gemm_launch<TILE, kHH | kHL | kLH>(ra, ral, mp, as, Xt[cur], bl, mp, xs, mp, Tn, 0, Tm * Tn, g.count,
+                                                g.cus, eap, st);
+    if (cs)
+      return gemm_launch<TILE, kHH | kLH>(ra, ral, mp, as, Xt[cur], nullptr, mp, xs, mp, Tn, 0, Tm * Tn, g.count,
+                                          g.cus, eap, st);
+    if (xlo)
+      return gemm_launch<TILE, kHH | kHL>(ra, nullptr, mp, as, Xt[cur], bl, mp, xs, mp, Tn, 0, Tm * Tn, g.count,
+                                          g.cus, eap, st);
+    return gemm_launch<TILE, kHH>(ra, nullptr, mp, as, Xt[cur], nullptr, mp, xs, mp, Tn, 0, Tm * Tn, g.count, g.cus,
+                                  eap, st);
+  };
   timer_begin(st);
-  if (cs && xlo)
-    e = gemm_launch<TILE, kHH | kHL | kLH>(ra, ral, mp, as, Xt[cur], bl, mp, xs, mp, Tn, 0, Tm * Tn, g.count, g.cus,
-                                           eap, st);
-  else if (cs)
-    e = gemm_launch<TILE, kHH | kLH>(ra, ral, mp, as, Xt[cur], nullptr, mp, xs, mp, Tn, 0, Tm * Tn, g.count, g.cus,
-                                     eap, st);
-  else if (xlo)
-    e = gemm_launch<TILE, kHH | kHL>(ra, nullptr, mp, as, Xt[cur], bl, mp, xs, mp, Tn, 0, Tm * Tn, g.count, g.cus,
-                                     eap, st);
+  if (last)
+    e = apply(EpiApplyBf16<PT, true>{g.tab, g.sc, X, xlo ? Xl : nullptr, Xt[cur ^ 1], rd, mp, np, g.m, g.n});
   else
-    e = gemm_launch<TILE, kHH>(ra, nullptr, mp, as, Xt[cur], nullptr, mp, xs, mp, Tn, 0, Tm * Tn, g.count, g.cus,
-                               eap, st);
+    e = apply(EpiApplyBf16<PT, false>{g.tab, g.sc, X, xlo ? Xl : nullptr, Xt[cur ^ 1], rd, mp, np, g.m, g.n});
   if (e != hipSuccess) return e;
   timer_end(st, alg, alg * prods);
   return hipSuccess;

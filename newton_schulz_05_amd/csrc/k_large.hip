@@ -368,12 +368,16 @@ struct NatStore {
   }
 };
 
-// Gram (bf16 path): A = sc2 * acc (upper tiles only: its only reader is the
-// poly epilogue at the same positions), plus its bf16 hi/lo split H, L, which
-// are GEMM operands and so are mirrored.  L is written only for steps whose
-// A^2 takes the split products (with_lo).
+// Gram (bf16 path): A = sc2 * acc as its bf16 hi/lo split H, L: H is a GEMM
+// operand and so mirrored, L is written on the upper tiles and mirrored when
+// A^2 takes the split products (with_lo).  The epilogues that read A at the
+// same positions (the poly's b A, the d A of T = P A) take H + L, which
+// holds A to about 16 mantissa bits.  Against an fp32 copy of A (and of T),
+// in an emulation of the GPU's rounding points, the error of O was the same
+// to two digits (lean recipe at 4096^2, precise at 1536 x 2048; rank m/8
+// and log-spaced spectra), and the planes move a third fewer bytes.
 struct EpiGramBf16 {
-  float* A; uint16_t* H; uint16_t* L; const float* scal; int use_scale; int with_lo; int64_t mp;
+  uint16_t* H; uint16_t* L; const float* scal; int use_scale; int with_lo; int64_t mp;
   static constexpr bool kCol = true;
   struct Uni { float s2; };
   struct In {};
@@ -390,9 +394,8 @@ struct EpiGramBf16 {
     }
     const int k0 = diag ? clamp_run(i - j0) : 0;  // diagonal tiles: j >= i
     const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
-    Seg<float>::store(A + o, k0, kRun, v);
     Seg<uint16_t>::store(H + o, k0, kRun, v);
-    if (with_lo) Seg<uint16_t>::store(L + o, k0, kRun, lo);
+    Seg<uint16_t>::store(L + o, k0, kRun, lo);
   }
   __device__ __forceinline__ void col(const Uni&, int z, int64_t j, int64_t i0, const float* v, bool diag,
                                       const In&) const {
@@ -406,17 +409,20 @@ struct EpiGramBf16 {
   }
 };
 
-// Poly (bf16 path): P = ps*(a I + b A + c S); off-diagonal bf16 (mirrored),
-// with its lo part bf16(P - hi) in PoffL when given, diagonal fp32 in Pd
+// Poly (bf16 path): P = ps*(a I + b A + c S), A read as its planes AH + AL;
+// off-diagonal bf16 (mirrored), with its lo part bf16(P - hi) in PoffL when
+// given, diagonal fp32 in Pd
 struct EpiPolyBf16 {
-  const float* A; uint16_t* Poff; uint16_t* PoffL; float* Pd; const float* scal; int use_scale;
-  float a, b, c; int64_t mp, m;
+  const uint16_t* AH; const uint16_t* AL; uint16_t* Poff; uint16_t* PoffL; float* Pd;
+  const float* scal; int use_scale; float a, b, c; int64_t mp, m;
   static constexpr bool kCol = true;
   struct Uni { float ps; };
-  struct In { Run<float> a; };
+  struct In { Run<uint16_t> h, l; };
   __device__ __forceinline__ Uni uni(int z) const { return Uni{use_scale ? scal[z * 4 + 0] : 1.0f}; }
   __device__ __forceinline__ void fetch(const Uni&, int z, int64_t i, int64_t j0, int64_t, int64_t, In& in) const {
-    in.a.fetch(A + int64_t(z) * mp * mp + i * mp + j0);
+    const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
+    in.h.fetch(AH + o);
+    in.l.fetch(AL + o);
   }
   __device__ __forceinline__ void row(const Uni& un, int z, int64_t i, int64_t j0, float* v, bool diag,
                                       const In& in) const {
@@ -426,7 +432,7 @@ struct EpiPolyBf16 {
     float pv[kRun];
 #pragma unroll
     for (int k = 0; k < kRun; ++k) {
-      float p = fmaf(c, v[k], b * in.a[k]);
+      float p = fmaf(c, v[k], b * (in.h[k] + in.l[k]));
       if (i == j0 + k) {
         p = ps * (p + a);
         Pd[int64_t(z) * mp + i] = (i < m) ? p : 0.f;
@@ -461,18 +467,20 @@ struct EpiPolyBf16 {
 
 // Grouped steps, m x m products of commuting symmetric matrices (bf16 path):
 // C = acc + d[i] * S[i][j], with acc = Poff B^T from the GEMM, d the fp32
-// diagonal of the left factor and S the right factor in fp32 (upper tiles).
-// Gives T = P_j A_j and A_{j+1} = P_j T.  C is stored in fp32 over S (same
-// position, same thread: in place), and as bf16 hi (and lo when with_lo),
-// mirrored to full matrices since they are GEMM operands.
+// diagonal of the left factor and S the right factor, read as its planes
+// SH + SL (upper tiles).  Gives T = P_j A_j and A_{j+1} = P_j T.  C is
+// stored as bf16 hi H, mirrored to a full matrix since it is a GEMM operand,
+// and lo L on the upper tiles (mirrored when with_lo).
 struct EpiSymMul {
-  float* S; const float* d; uint16_t* H; uint16_t* L; int with_lo; int64_t mp;
+  const uint16_t* SH; const uint16_t* SL; const float* d; uint16_t* H; uint16_t* L; int with_lo; int64_t mp;
   static constexpr bool kCol = true;
   struct Uni {};
-  struct In { Run<float> s; float d; };
+  struct In { Run<uint16_t> h, l; float d; };
   __device__ __forceinline__ Uni uni(int) const { return Uni{}; }
   __device__ __forceinline__ void fetch(const Uni&, int z, int64_t i, int64_t j0, int64_t, int64_t, In& in) const {
-    in.s.fetch(S + int64_t(z) * mp * mp + i * mp + j0);
+    const int64_t o = int64_t(z) * mp * mp + i * mp + j0;
+    in.h.fetch(SH + o);
+    in.l.fetch(SL + o);
     in.d = d[int64_t(z) * mp + i];
   }
   __device__ __forceinline__ void row(const Uni&, int z, int64_t i, int64_t j0, float* v, bool diag,
@@ -482,12 +490,11 @@ struct EpiSymMul {
     float lo[kRun];
 #pragma unroll
     for (int k = 0; k < kRun; ++k) {
-      v[k] = fmaf(in.d, in.s[k], v[k]);
+      v[k] = fmaf(in.d, in.h[k] + in.l[k], v[k]);
       lo[k] = v[k] - bf2f(f2bf(v[k]));
     }
-    Seg<float>::store(S + o, k0, kRun, v);
     Seg<uint16_t>::store(H + o, k0, kRun, v);
-    if (with_lo) Seg<uint16_t>::store(L + o, k0, kRun, lo);
+    Seg<uint16_t>::store(L + o, k0, kRun, lo);
   }
   __device__ __forceinline__ void col(const Uni&, int z, int64_t j, int64_t i0, const float* v, bool diag,
                                       const In&) const {
@@ -1159,11 +1166,11 @@ static inline bool split_a2(int64_t m, int k, int steps) {
 // one Gram and one apply.  Every P_j, A_j and product below is a polynomial
 // in A_k, so they commute and the products are symmetric (upper tiles,
 // mirrored).  For j = 0 .. G-1:
-//   j = 0   Gram  A_0 = sc X X^T                  -> A fp32 (upper), H (+ L)
+//   j = 0   Gram  A_0 = sc X X^T                  -> H, L
 //           poly  P_0 = a I + b A_0 + c A_0^2     -> Pb[0] (scaled by s only
 //                 when G = 1 and k = 0)
-//   j >= 1  T     T = P_{j-1} A_{j-1}             -> fp32 over A, Th (+ Tl)
-//           A'    A_j = P_{j-1} T                 -> fp32 over A, H (+ L)
+//   j >= 1  T     T = P_{j-1} A_{j-1}             -> Th, Tl
+//           A'    A_j = P_{j-1} T                 -> H, L
 //           poly  P_j from A_j                    -> Pb[j % 2]
 //           R     R_j = P_j R_{j-1}, R_0 = s P_0  -> Rb[j % 2] (off-diagonal
 //                 bf16, diagonal fp32; s only when k = 0)
@@ -1194,14 +1201,13 @@ static hipError_t ns_group_bf16(const LargeArgs& g, hipStream_t st, int k, int G
   uint16_t* Xt[2] = {(uint16_t*)(ws + L.xt0), (uint16_t*)(ws + L.xt1)};
   uint16_t* Xl = (uint16_t*)(ws + L.xl);
   uint16_t* Xtl = (uint16_t*)(ws + L.xtl);
-  float* A = (float*)(ws + L.a);
   float* scal = (float*)(ws + L.scal);
   uint16_t* H = (uint16_t*)(ws + L.h);
   uint16_t* Lo = (uint16_t*)(ws + L.l);
   uint16_t* Th = (uint16_t*)(ws + L.th);
   // the lean recipe holds up to kLeanMaxSteps steps; beyond, the precise chain
   const bool cs = g.precise || g.sc.ns_steps > kLeanMaxSteps;
-  uint16_t* Tl = cs ? (uint16_t*)(ws + L.tl) : nullptr;
+  uint16_t* Tl = (uint16_t*)(ws + L.tl);
   uint16_t* Pb[2] = {(uint16_t*)(ws + L.poff), (uint16_t*)(ws + L.poff2)};
   uint16_t* PbL[2] = {cs ? (uint16_t*)(ws + L.poffl0) : nullptr, cs ? (uint16_t*)(ws + L.poffl1) : nullptr};
   float* Pdb[2] = {(float*)(ws + L.pdiag), (float*)(ws + L.pdiag2)};
@@ -1226,11 +1232,11 @@ static hipError_t ns_group_bf16(const LargeArgs& g, hipStream_t st, int k, int G
   auto poly = [&](int j) {
     const bool sp = split_a2(g.m, k + j, steps);
     uint16_t* pl = (cs || G == 1) ? PbL[j & 1] : nullptr;
-    EpiPolyBf16 ep{A, Pb[j & 1], pl, Pdb[j & 1], scal, (G == 1 && k == 0) ? 1 : 0, g.sc.a, g.sc.b, g.sc.c, mp, g.m};
+    EpiPolyBf16 ep{H, Lo, Pb[j & 1], pl, Pdb[j & 1], scal, (G == 1 && k == 0) ? 1 : 0, g.sc.a, g.sc.b, g.sc.c, mp, g.m};
     return sp ? sym3(H, Lo, H, Lo, ep) : sym1(H, H, ep);
   };
   // Gram: with X_0's lo plane in the precise recipe, X X^T ~ Xh Xh^T + Xh Xl^T + Xl Xh^T
-  EpiGramBf16 eg{A, H, Lo, scal, k == 0, (split_a2(g.m, k, steps) || cs) ? 1 : 0, mp};
+  EpiGramBf16 eg{H, Lo, scal, k == 0, (split_a2(g.m, k, steps) || cs) ? 1 : 0, mp};
   e = (xlo && cs) ? gemm_launch<TILE, kHH | kHL | kLH>(X, Xl, np, xs, X, Xl, np, xs, np, Tm, 1, up, g.count, g.cus,
                                                        eg, st)
                   : gemm_launch<TILE, kHH>(X, nullptr, np, xs, X, nullptr, np, xs, np, Tm, 1, up, g.count, g.cus, eg, st);
@@ -1238,9 +1244,10 @@ static hipError_t ns_group_bf16(const LargeArgs& g, hipStream_t st, int k, int G
   if ((e = poly(0)) != hipSuccess) return e;
   for (int j = 1; j < G; ++j) {
     const int pp = (j - 1) & 1;  // P_{j-1}
-    EpiSymMul et{A, Pdb[pp], Th, Tl, cs ? 1 : 0, mp};
+    // T = P A from A's planes into T's, A' = P T from T's planes into A's
+    EpiSymMul et{H, Lo, Pdb[pp], Th, Tl, cs ? 1 : 0, mp};
     if ((e = cs ? sym3(Pb[pp], PbL[pp], H, Lo, et) : sym1(Pb[pp], H, et)) != hipSuccess) return e;
-    EpiSymMul ea{A, Pdb[pp], H, Lo, (split_a2(g.m, k + j, steps) || cs) ? 1 : 0, mp};
+    EpiSymMul ea{Th, Tl, Pdb[pp], H, Lo, (split_a2(g.m, k + j, steps) || cs) ? 1 : 0, mp};
     if ((e = cs ? sym3(Pb[pp], PbL[pp], Th, Tl, ea) : sym1(Pb[pp], Th, ea)) != hipSuccess) return e;
     if ((e = poly(j)) != hipSuccess) return e;
     // R_j = P_j R_{j-1}; R_0 = s P_0 is P_0 itself with the scale applied here

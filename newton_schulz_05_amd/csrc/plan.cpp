@@ -46,6 +46,8 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
   L.x = take(xb);
   L.xt0 = take(xb);
   L.xt1 = take(xb);
+  // fp32 A of the fp32 path; the bf16 path holds A as H + L and leaves this
+  // region unused (kept, so the chunking of a group does not depend on it)
   L.a = take(size_t(count) * size_t(mp) * size_t(mp) * 4);
   if (param_dt == MUON_BF16) {
     L.h = take(size_t(count) * size_t(mp) * size_t(mp) * 2);

@@ -924,9 +924,9 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
       }
     }
   };
-  auto mfma_slice = [&](int q) {
+  auto mfma_slice = [&](int q, int a0, int a1) {
 #pragma unroll
-    for (int a = 0; a < G::FM; ++a)
+    for (int a = a0; a < a1; ++a)
 #pragma unroll
       for (int b = 0; b < G::FN; ++b) {
         acc[a][b] = mfma32x32x16(fa[q][0][a], fb[q][0][b], acc[a][b]);
@@ -934,17 +934,21 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
         if constexpr ((PR & kLH) != 0) acc[a][b] = mfma32x32x16(fa[q][NA - 1][a], fb[q][0][b], acc[a][b]);
       }
   };
-  // a k-tile in stage st: all its fragment reads and the MFMAs of all but
-  // its last k slice (head), then the last slice from registers (tail)
+  // a k-tile in stage st: all its fragment reads and three quarters of its
+  // MFMAs (head), then the last quarter from registers (tail): the last k
+  // slice when there are 4, the second half of the last slice's rows of
+  // MFMA tiles when there are 2
+  constexpr int TA = (KS >= 4) ? 0 : G::FM / 2;
   auto head = [&](int st) {
     lread(st, 0, 0);
 #pragma unroll
     for (int ks = 0; ks + 1 < KS; ++ks) {
       lread(st, ks + 1, (ks + 1) & 1);
-      mfma_slice(ks & 1);
+      mfma_slice(ks & 1, 0, G::FM);
     }
+    mfma_slice((KS - 1) & 1, 0, TA);
   };
-  auto tail = [&]() { mfma_slice((KS - 1) & 1); };
+  auto tail = [&]() { mfma_slice((KS - 1) & 1, TA, G::FM); };
   // stage st's loads have landed and every wave has read the other stage
   auto stage_sync = [&]() {
     __builtin_amdgcn_sched_barrier(0);
@@ -954,13 +958,15 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
   };
 
   // Two stages: the loads of k-tile t+1 fly while k-tile t is multiplied.
-  // Each k-tile's last slice is multiplied after the barrier that frees its
-  // stage, once the next loads into that stage are issued, so the waves
+  // A quarter of each k-tile's MFMAs is issued after the barrier that frees
+  // its stage, once the next loads into that stage are issued, so the waves
   // have MFMAs to issue while those loads start (the order of the products
   // into each accumulator is unchanged).  The scheduling barriers fix this
   // order: left to itself the compiler moved a varying share of a stage's
   // MFMAs below the wait, up to all of them in one build of the three-plane
-  // apply (10% slower).  KT is even (K is a multiple of 128): the loop body
+  // apply (10% slower); none (every MFMA before the wait) was 1-2% slower
+  // than its own choice, a quarter 3-10% faster on the single-product
+  // launches and the same on the three-product ones.  KT is even (K is a multiple of 128): the loop body
   // is straight-line code over a pair of k-tiles, the last pair peeled.
   const int KT = int(K / BK);
   gload(0, 0);

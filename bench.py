@@ -41,8 +41,8 @@ TRAFFIC = {
            "fetch_kib_per_dispatch": 83727.4, "write_kib_per_dispatch": 109375.8,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
-           "kernel_source_sha256": "7967fbf1368cbcf17533fe19d7459d34e0883de5c215939d90aea5e9a3882cad",
-           "fetch_kib_per_dispatch": 12438558.8, "write_kib_per_dispatch": 1640442.6,
+           "kernel_source_sha256": "dc85e2d02d7ee37756ac7ecba9812fb3ff06e9e0c0d3b6d9b9addd5e18115b75",
+           "fetch_kib_per_dispatch": 12369880.7, "write_kib_per_dispatch": 1634056.2,
            "fetch_scale": 2.0, "write_scale": 1.0},
 }
 

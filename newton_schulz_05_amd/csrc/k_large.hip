@@ -828,7 +828,10 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
   constexpr int NW = G::NT / 64;
   constexpr int LP = PLANE / G::NT;             // loads per thread per plane
   constexpr int KS = BK / 16;
-  __shared__ u16x8 lds[2][NPL][PLANE];          // [stage][Ah, (Al), Bh, (Bl)]
+  // three planes at BK = 32 (the applies with a lo plane on one side) take a
+  // ring of three stages, 144 KB; two or four planes two stages, 128 KB
+  constexpr int NST = (NPL == 3 && TILE == 256) ? 3 : 2;
+  __shared__ u16x8 lds[NST][NPL][PLANE];        // [stage][Ah, (Al), Bh, (Bl)]
   // Work items w = blockIdx.x, blockIdx.x + gridDim.x, ... < nwork: a full
   // grid stays resident (one round of workgroups) and each workgroup takes
   // its next tile after its epilogue, so the rounds of the CUs drift apart
@@ -969,6 +972,80 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
   // launches and the same on the three-product ones.  KT is even (K is a multiple of 128): the loop body
   // is straight-line code over a pair of k-tiles, the last pair peeled.
   const int KT = int(K / BK);
+  if constexpr (NST == 3) {
+    // Three stages: the loads of k-tiles t+1 and t+2 fly while k-tile t is
+    // multiplied, so a load has two k-tiles' MFMAs (~2 us) to arrive instead
+    // of one (the three-plane apply of the 8192 x 28672 pair 13.2 -> 12.5 ms,
+    // bitwise identical).  The loads are written as inline asm (M0 = the
+    // LDS destination, then the buffer load with the lds modifier; no
+    // register is written, so nothing of the asm's stays live) and waited
+    // for with explicit vmcnt counts: issued through the builtin, the
+    // compiler would wait for every load in flight before each barrier and
+    // before every fragment read of another stage, which undoes the ring.
+    // No other vector memory access is issued in this loop, and the last
+    // wait is vmcnt(0), so the compiler's own counts stay valid after it.
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    i32x4_t rv[NPL];
+#pragma unroll
+    for (int s = 0; s < NPL; ++s) {
+      const uint64_t ga = (uint64_t)(uintptr_t)gsrc[s];
+      rv[s] = i32x4_t{int(__builtin_amdgcn_readfirstlane(uint32_t(ga))),
+                      int(__builtin_amdgcn_readfirstlane(uint32_t(ga >> 32) & 0xffffu)),
+                      int(uint32_t(TILE * ((s < NA) ? lda : ldb) * 2)), 0x00020000};
+    }
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane(
+        uint32_t((uintptr_t)(__attribute__((address_space(3))) u16x8*)(&lds[0][0][0])));
+    constexpr int NL = NPL * LP;  // loads per k-tile and thread
+    auto gload3 = [&](int64_t k0, int st) {
+#pragma unroll
+      for (int s = 0; s < NPL; ++s) {
+        const int64_t ld = (s < NA) ? lda : ldb;
+#pragma unroll
+        for (int p = 0; p < LP; ++p) {
+          const int soff = __builtin_amdgcn_readfirstlane(int((int64_t((p * NW + wvu) * RL) * ld + k0) * 2));
+          const uint32_t m0v = lbase + uint32_t(((st * NPL + s) * PLANE + (p * NW + wvu) * 64) * 16);
+          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                       :: "s"(m0v), "v"(voff[s < NA ? 0 : 1]), "s"(rv[s]), "s"(soff) : "memory", "m0");
+        }
+      }
+    };
+    auto bar3 = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    gload3(0, 0);
+    gload3(BK, 1);
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NL) : "memory");  // k-tile 0 in stage 0
+    bar3();
+    gload3(2 * BK, 2);
+    head(0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NL) : "memory");  // k-tile 1 in stage 1
+    bar3();
+    int sr = 1, sd = 0;
+    for (int kt = 1; kt + 2 < KT; ++kt) {
+      gload3(int64_t(kt + 2) * BK, sd);   // into the stage k-tile kt - 1 used
+      tail();                             // k-tile kt - 1
+      head(sr);                           // k-tile kt
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NL) : "memory");  // k-tile kt + 1 landed
+      bar3();
+      sr = (sr == 2) ? 0 : sr + 1;
+      sd = (sd == 2) ? 0 : sd + 1;
+    }
+    tail();                               // k-tile KT - 3
+    head(sr);                             // k-tile KT - 2
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    bar3();
+    sr = (sr == 2) ? 0 : sr + 1;
+    tail();
+    head(sr);                             // k-tile KT - 1
+    tail();
+  } else {
   gload(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -988,6 +1065,7 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
   tail();                             // k-tile KT - 2
   head(1);                            // k-tile KT - 1
   tail();
+  }
 
   // Epilogue: each wave stages one 32 x 32 MFMA tile at a time in its own LDS
   // slot (the operand stages are free now) and reads it back as row runs and

@@ -41,8 +41,8 @@ TRAFFIC = {
            "fetch_kib_per_dispatch": 83727.4, "write_kib_per_dispatch": 109375.8,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
-           "kernel_source_sha256": "dc85e2d02d7ee37756ac7ecba9812fb3ff06e9e0c0d3b6d9b9addd5e18115b75",
-           "fetch_kib_per_dispatch": 12369880.7, "write_kib_per_dispatch": 1634056.2,
+           "kernel_source_sha256": "8660f16083c71e579fef3cc10044fb2244d5ebf3638122a9691c3311ae2a0cf9",
+           "fetch_kib_per_dispatch": 12631971.7, "write_kib_per_dispatch": 1639159.7,
            "fetch_scale": 2.0, "write_scale": 1.0},
 }
 

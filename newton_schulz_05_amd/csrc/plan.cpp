@@ -16,10 +16,8 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // Split `count` matrices into the fewest chunks of at most `cap` each, with
 // sizes as even as possible (the split never changes any result: every matrix
 // is computed the same way in any chunk).
-std::vector<Chunk> split_even(int32_t count, int32_t cap) {
+std::vector<Chunk> split_n(int32_t count, int32_t n) {
   std::vector<Chunk> out;
-  if (cap < 1) cap = 1;
-  int32_t n = (count + cap - 1) / cap;
   int32_t base = count / n, extra = count % n, first = 0;
   for (int32_t i = 0; i < n; ++i) {
     int32_t c = base + (i < extra ? 1 : 0);
@@ -27,6 +25,30 @@ std::vector<Chunk> split_even(int32_t count, int32_t cap) {
     first += c;
   }
   return out;
+}
+
+std::vector<Chunk> split_even(int32_t count, int32_t cap) {
+  if (cap < 1) cap = 1;
+  return split_n(count, (count + cap - 1) / cap);
+}
+
+// The MFMA path's chunks: the fewest of at most `cap` matrices, unless up to
+// three more leave fewer symmetric tiles (sym per matrix) in partial last
+// rounds of kRoundTiles, which run as a second launch at half the tile size
+// and a lower rate; ties go to fewer chunks.  The 32-layer set's wide group
+// (96 x [4096, 14336], 136 tiles a matrix) takes 3 chunks of 32, 17 whole
+// rounds each, instead of 4 of 24 with 192 tiles left over in each.
+std::vector<Chunk> split_rounds(int32_t count, int32_t cap, int64_t sym) {
+  if (cap < 1) cap = 1;
+  const int32_t n0 = (count + cap - 1) / cap;
+  int32_t best = n0;
+  int64_t best_left = -1;
+  for (int32_t n = n0; n <= std::min(count, n0 + 3); ++n) {
+    int64_t left = 0;
+    for (const Chunk& c : split_n(count, n)) left += (int64_t(c.count) * sym) % kRoundTiles;
+    if (best_left < 0 || left < best_left) { best = n; best_left = left; }
+  }
+  return split_n(count, best);
 }
 
 }  // namespace
@@ -46,9 +68,8 @@ LargeLayout large_layout(const Group& g, int32_t count, muon_dtype param_dt) {
   L.x = take(xb);
   L.xt0 = take(xb);
   L.xt1 = take(xb);
-  // fp32 A of the fp32 path; the bf16 path holds A as H + L and leaves this
-  // region unused (kept, so the chunking of a group does not depend on it)
-  L.a = take(size_t(count) * size_t(mp) * size_t(mp) * 4);
+  // fp32 A (the fp32 path; the bf16 path holds A as its planes H + L)
+  L.a = (param_dt == MUON_BF16) ? 0 : take(size_t(count) * size_t(mp) * size_t(mp) * 4);
   if (param_dt == MUON_BF16) {
     L.h = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
     L.l = take(size_t(count) * size_t(mp) * size_t(mp) * 2);
@@ -226,7 +247,12 @@ muon_status build_plan(const muon_shape* shapes, int32_t n_params, muon_dtype pa
       LargeLayout one = large_layout(g, 1, param_dt);
       int32_t cap = (int32_t)std::max<size_t>(1, kChunkBytesCap / std::max<size_t>(one.bytes, 1));
       cap = std::min(cap, kMaxChunkMats);
-      g.chunks = split_even(count, cap);
+      if (g.path == PATH_MFMA) {
+        const int64_t tm = g.mp / g.tile;
+        g.chunks = split_rounds(count, cap, tm * (tm + 1) / 2);
+      } else {
+        g.chunks = split_even(count, cap);
+      }
     }
     for (const Chunk& c : g.chunks) g.max_chunk = std::max(g.max_chunk, c.count);
     size_t need = (g.path == PATH_SKINNY) ? skinny_bytes(g, g.max_chunk)

@@ -40,7 +40,8 @@ constexpr int64_t kMfmaTileBig = 256;        // MFMA path: tile for groups with 
 constexpr int64_t kF32Tile = 64;             // row/column padding of the fp32 path
 constexpr int64_t kMomTile = 64;             // momentum kernel tile (rows and columns)
 constexpr size_t kSyncBytes = 8192;          // barrier counters (skinny path)
-constexpr size_t kChunkBytesCap = size_t(24) << 30;  // workspace bytes one chunk may use
+constexpr size_t kChunkBytesCap = size_t(32) << 30;  // workspace bytes one chunk may use
+constexpr int64_t kRoundTiles = 256;         // MFMA path: tiles of one round (one per CU)
 constexpr int kMaxChunkMats = 80;            // must equal kMaxChunk in common.hpp
 
 struct MatEntry {

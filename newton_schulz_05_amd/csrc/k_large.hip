@@ -1004,8 +1004,13 @@ __global__ __launch_bounds__(GemmGeom<TILE>::NT, GemmGeom<TILE>::PER_CU) void ge
         for (int p = 0; p < LP; ++p) {
           const int soff = __builtin_amdgcn_readfirstlane(int((int64_t((p * NW + wvu) * RL) * ld + k0) * 2));
           const uint32_t m0v = lbase + uint32_t(((st * NPL + s) * PLANE + (p * NW + wvu) * 64) * 16);
+          // M0 is declared clobbered; these kernels use it nowhere else (the
+          // compiler warns that a reserved register is not preserved)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
           asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                        :: "s"(m0v), "v"(voff[s < NA ? 0 : 1]), "s"(rv[s]), "s"(soff) : "memory", "m0");
+#pragma clang diagnostic pop
         }
       }
     };

@@ -42,7 +42,7 @@ TRAFFIC = {
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
            "kernel_source_sha256": "46e3f63396f0cba7517f653e5902ce362e1ab2faf2af81cc36f803bb104613cf",
-           "fetch_kib_per_dispatch": 12631971.7, "write_kib_per_dispatch": 1639159.7,
+           "fetch_kib_per_dispatch": 12586613.7, "write_kib_per_dispatch": 1637869.7,
            "fetch_scale": 2.0, "write_scale": 1.0},
 }
 

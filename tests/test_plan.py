@@ -47,6 +47,22 @@ def test_c4_merges_transposed_up_gate_with_down():
     assert g[(4096, 4096)]["n_chunks"] >= 2
 
 
+def test_mfma_chunks_leave_no_partial_round_when_they_can():
+    # 256-tiles: 136 symmetric tiles per 4096-row matrix.  128 squares fit
+    # 4 chunks of 32 (4352 tiles, 17 rounds of 256); the 96 wide matrices
+    # fit 3 of 32 under the workspace cap, where the fewest chunks alone
+    # would do too (one more chunk is taken only when it leaves fewer tiles
+    # over, and 3 x 32 leaves none)
+    plan = MuonPlan(W.WORKLOADS["c4"].shapes, torch.bfloat16)
+    g = {(x["m"], x["n"]): x for x in plan.groups()}
+    assert g[(4096, 4096)]["n_chunks"] == 4
+    assert g[(4096, 14336)]["n_chunks"] == 3
+    # the workspace holds the largest chunk of any group, under the 32 GiB cap
+    assert plan.workspace_bytes <= (32 << 30) + (1 << 20)
+    # a group that one chunk holds stays in one chunk
+    assert [x["n_chunks"] for x in MuonPlan([(2048, 2048)] * 10, torch.bfloat16).groups()] == [1]
+
+
 def test_c1_c2_c5_groups():
     assert [(x["m"], x["n"], x["count"]) for x in MuonPlan(W.WORKLOADS["c1"].shapes, torch.float32).groups()] \
         == [(64, 128, 4)]

@@ -43,7 +43,9 @@
  *     the caller.  The step entry points allocate and free nothing on the
  *     device and never synchronise the host with the device; they enqueue
  *     work on `stream` (a hipStream_t passed as void*, NULL = null stream)
- *     and return.
+ *     and return.  Part of a small group's work may run on the plan's side
+ *     stream, which `stream` waits for within the call (muon_set_side_stream),
+ *     so every call's work is ordered on `stream` as if it all ran there.
  *   - Pointer arguments named `*_ptrs` are HOST arrays of DEVICE pointers,
  *     one per parameter, in plan order.
  *   - Every tensor is dense row-major [batch, rows, cols], 16-byte aligned,
@@ -53,7 +55,9 @@
  *     launch failed after work may have been enqueued: buffer contents are
  *     then unspecified.
  *   - muon_last_error_detail() gives a thread-local text for the last error.
- *   - A plan holds only host metadata; it may be used from several host
+ *   - A plan holds host metadata, and (after its first eager step on a
+ *     device, for plans with MFMA groups) one side stream and two events
+ *     there, see muon_set_side_stream; it may be used from several host
  *     threads one call at a time.  Two calls that share a workspace must be
  *     ordered on one stream (the workspace holds per-call state).
  */
@@ -110,6 +114,8 @@ typedef struct muon_plan_s* muon_plan;
 muon_status muon_plan_create(const muon_shape* shapes, int32_t n_params, muon_dtype param_dt,
                              muon_dtype grad_dt, muon_dtype mom_dt, muon_plan* out);
 
+/* Frees the plan, with its side streams and events (work still queued on a
+ * side stream completes before they are released). */
 void muon_plan_destroy(muon_plan plan);
 
 /* Bytes of device workspace muon_step / muon_ns need for this plan. */
@@ -282,6 +288,21 @@ muon_status muon_workspace_status(muon_plan plan, void* workspace, size_t worksp
  * follow in this process (default 1048576, about a second; 0 restores the
  * default).  Meant for tests of the timeout path. */
 void muon_set_wait_limit(uint32_t polls);
+
+/* Whether the calls that follow in this process may run part of a small
+ * MFMA group's work on the plan's side stream (on by default; 0 turns it
+ * off).  It changes only which launches may run at the same time, never a
+ * result bit.  A group of several NS steps forms R_j = P_j R_{j-1} beside
+ * the next step's products when its m x m launches leave compute units idle
+ * (fewer 256-tiles than CUs): the Newton-Schulz steps of item 1(1) of the
+ * HyperParallel FSDP Muon optimizer RFC, for a batch too small to fill the
+ * device.  The side stream (default priority) and its two events are made
+ * on the plan's first eager muon_step or muon_ns on a device (not while the
+ * stream is captured, and not by muon_step_noalloc, whose launches all stay
+ * on its stream) and released by muon_plan_destroy; the launch stream waits
+ * for the side stream before the group's apply, so when a call returns
+ * control all of its work is ordered on `stream`.  Thread-safe. */
+void muon_set_side_stream(int32_t enable);
 
 /* ---- Kernel timing for benchmarks ----------------------------------------
  * While enabled, every apply of the MFMA path (X' = P X or R X: the largest

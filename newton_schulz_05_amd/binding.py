@@ -34,7 +34,8 @@ STATUS = {
 EXPORTS = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes",
            "muon_plan_num_groups", "muon_plan_group_info", "muon_step", "muon_ns",
            "muon_plan_num_matrices", "muon_plan_assign", "muon_shard_update", "muon_adamw_step",
-           "muon_workspace_status", "muon_set_wait_limit", "muon_poll_timeout", "muon_step_noalloc",
+           "muon_workspace_status", "muon_set_wait_limit", "muon_set_side_stream", "muon_poll_timeout",
+           "muon_step_noalloc",
            "muon_kernel_timing", "muon_kernel_timing_read",
            "muon_status_str", "muon_last_error_detail", "muon_version"]
 
@@ -99,6 +100,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_workspace_status.restype = i32
     lib.muon_set_wait_limit.argtypes = [ctypes.c_uint32]
     lib.muon_set_wait_limit.restype = None
+    lib.muon_set_side_stream.argtypes = [i32]
+    lib.muon_set_side_stream.restype = None
     lib.muon_poll_timeout.argtypes = [P(i32)]
     lib.muon_poll_timeout.restype = i32
     lib.muon_kernel_timing.argtypes = [i32]
@@ -436,6 +439,12 @@ def set_wait_limit(polls: int) -> None:
     """Polls before a waiting workgroup of the skinny kernel gives up
     (muon_set_wait_limit; 0 restores the default)."""
     load_library().muon_set_wait_limit(int(polls))
+
+
+def set_side_stream(enable: bool) -> None:
+    """Whether small MFMA groups may run their R chain on the plan's side
+    stream (muon_set_side_stream; on by default, never changes a result)."""
+    load_library().muon_set_side_stream(1 if enable else 0)
 
 
 class BoundNS:

@@ -2,7 +2,10 @@
 // tables, and the launch sequence on the caller's stream.  The step entry
 // points allocate and free no device memory and never wait for the device;
 // the only allocation is one 4-byte pinned host word per device, made on the
-// first eager step (the skinny path's timeout report).
+// first eager step (the skinny path's timeout report).  A plan with MFMA
+// groups also creates, on its first eager step on a device, one stream and
+// two events there (the side stream of small groups' product chains), and
+// releases them when it is destroyed.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -17,8 +20,36 @@
 #include "plan.hpp"
 #include "validate.hpp"
 
+// A second stream on one device with the events that fork work onto it from
+// the launch stream and join it back (kernels' launches, not the results,
+// depend on it: see ns_group_bf16).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false;  // creation attempted (it is not retried after a failure)
+};
+constexpr int kMaxDevices = 64;
+
 struct muon_plan_s {
   muon::Plan p;
+  SideStream side[kMaxDevices];  // per device, made on the plan's first eager step there
+  ~muon_plan_s() {
+    bool any = false;
+    for (const SideStream& ss : side) any = any || ss.s || ss.fork || ss.join;
+    if (!any) return;  // no HIP call for a plan that never made one
+    int cur = -1;
+    const bool have = hipGetDevice(&cur) == hipSuccess;
+    for (int d = 0; d < kMaxDevices; ++d) {
+      SideStream& ss = side[d];
+      if (!ss.s && !ss.fork && !ss.join) continue;
+      if (hipSetDevice(d) != hipSuccess) continue;
+      // work still queued on the stream completes before its resources go
+      if (ss.join) (void)hipEventDestroy(ss.join);
+      if (ss.fork) (void)hipEventDestroy(ss.fork);
+      if (ss.s) (void)hipStreamDestroy(ss.s);
+    }
+    if (have) (void)hipSetDevice(cur);
+  }
 };
 
 namespace {
@@ -55,13 +86,13 @@ bool capturing(hipStream_t st) {
 // capacity, and a host-visible word (pinned host memory) that a skinny
 // workgroup sets when one of its waits times out.
 struct DevState {
+  int index = -1;                 // device ordinal
   int cus = -1;
   int skinny_cap = -1;
   uint32_t* host_flag = nullptr;  // hipHostMalloc'd, 4 bytes; null until first eager step
   bool flag_tried = false;
   void* scratch = nullptr;        // device address of this device's copy of `scratch`
 };
-constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
 DevState g_dev[kMaxDevices];  // fixed storage: looking a device up allocates nothing
 
@@ -91,7 +122,42 @@ muon_status device_state(bool allow_alloc, DevState* out) {
     }
   }
   *out = d;
+  out->index = dev;
   return MUON_OK;
+}
+
+// Whether small groups may run a product chain on a plan's side stream
+// (muon_set_side_stream; on by default).
+std::atomic<bool> g_side_enabled{true};
+
+// The plan's side stream on the current device, made on first use when
+// `allow_alloc` (never while `st` is being captured: a recorded step keeps
+// every launch on the captured stream), or null.  Plans without MFMA groups
+// never make one.
+SideStream* side_stream(muon_plan plan, const DevState& dev, hipStream_t st, bool allow_alloc) {
+  if (!plan || !g_side_enabled.load() || capturing(st)) return nullptr;
+  SideStream& ss = plan->side[dev.index];
+  if (!ss.tried && allow_alloc) {
+    ss.tried = true;
+    bool mfma = false;
+    for (const muon::Group& grp : plan->p.groups) mfma = mfma || grp.path == muon::PATH_MFMA;
+    if (mfma) {
+      // default priority, and not synchronised with the null stream (the
+      // events order it against the launch stream)
+      const bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
+                      hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+                      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+      if (!ok) {
+        if (ss.join) (void)hipEventDestroy(ss.join);
+        if (ss.fork) (void)hipEventDestroy(ss.fork);
+        if (ss.s) (void)hipStreamDestroy(ss.s);
+        ss = SideStream{};
+        ss.tried = true;
+        (void)hipGetLastError();  // the failure changes nothing but the schedule
+      }
+    }
+  }
+  return ss.s ? &ss : nullptr;
 }
 
 // Reads and clears the host-visible timeout word of the current device.
@@ -119,7 +185,8 @@ size_t elem_size(muon_dtype d) { return d == MUON_BF16 ? 2 : 4; }
 // Enqueue every chunk of every group (arguments already validated).  `w`,
 // `g`, `m` are per-parameter device pointers (m may be null for muon_ns).
 muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, void* const* m,
-                    const muon::StepScalars& sc, void* workspace, hipStream_t st, const DevState& dev) {
+                    const muon::StepScalars& sc, void* workspace, hipStream_t st, const DevState& dev,
+                    const SideStream* side) {
   using namespace muon;
   uint8_t* ws = (uint8_t*)workspace;
   const size_t pes = elem_size(P.param_dt);
@@ -179,6 +246,9 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
         a.precise = grp.precise;
         a.x0_lo = a.bf16 && sc.mode == 0;  // muon_ns inputs are bf16 already: no lo part
         a.cus = dev.cus;
+        a.side = side ? side->s : nullptr;
+        a.ev_fork = side ? side->fork : nullptr;
+        a.ev_join = side ? side->join : nullptr;
         e = run_large(a, st);
       }
       if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -188,8 +258,9 @@ muon_status run_all(const muon::Plan& P, void* const* w, const void* const* g, v
 }
 
 // Device checks, the timeout report of earlier calls, then the launches.
-// `allow_alloc`: the host-visible timeout word may be allocated (first call).
-muon_status enqueue(const muon::Plan& P, void* const* w, const void* const* g, void* const* m,
+// `allow_alloc`: the host-visible timeout word and the plan's side stream may
+// be made (first eager call); `plan` null: no side stream.
+muon_status enqueue(muon_plan plan, const muon::Plan& P, void* const* w, const void* const* g, void* const* m,
                     const muon::StepScalars& sc, void* workspace, hipStream_t st, bool allow_alloc = true) {
   DevState dev;
   if (muon_status s = device_state(allow_alloc && !capturing(st), &dev); s != MUON_OK) return s;
@@ -198,7 +269,8 @@ muon_status enqueue(const muon::Plan& P, void* const* w, const void* const* g, v
     return fail(MUON_ERR_TIMEOUT, "an earlier skinny-path launch on this device timed out waiting for its "
                                   "workgroups; its W (or O) was left partly unwritten and its momenta were "
                                   "updated (nothing was enqueued by this call)");
-  return run_all(P, w, g, m, sc, workspace, st, dev);
+  const SideStream* side = side_stream(plan, dev, st, allow_alloc);
+  return run_all(P, w, g, m, sc, workspace, st, dev, side);
 }
 
 // ---- The allocation-free step (muon_step_noalloc) --------------------------
@@ -393,6 +465,8 @@ muon_status muon_workspace_status(muon_plan plan, void* workspace, size_t worksp
 
 void muon_set_wait_limit(uint32_t polls) { g_spin_limit.store(polls ? polls : kSpinLimit); }
 
+void muon_set_side_stream(int32_t enable) { g_side_enabled.store(enable != 0); }
+
 muon_status muon_poll_timeout(int32_t* timed_out) {
   if (!timed_out) return fail(MUON_ERR_INVALID_ARG, "null output pointer");
   *timed_out = 0;
@@ -412,7 +486,7 @@ muon_status muon_step(muon_plan plan, void* const* param_ptrs, const void* const
                                       a, b, c, ns_steps, scale, workspace, workspace_bytes, &d);
   if (s != MUON_OK) return fail(s, d);
   muon::StepScalars sc{lr, mu, wd, scale, a, b, c, nesterov, ns_steps, 0};
-  return enqueue(*P, param_ptrs, grad_ptrs, mom_ptrs, sc, workspace, (hipStream_t)stream);
+  return enqueue(plan, *P, param_ptrs, grad_ptrs, mom_ptrs, sc, workspace, (hipStream_t)stream);
 }
 
 muon_status muon_step_noalloc(muon_plan plan, void* const* param_ptrs, const void* const* grad_ptrs,
@@ -433,7 +507,8 @@ muon_status muon_step_noalloc(muon_plan plan, void* const* param_ptrs, const voi
   void* ws = nullptr;
   if ((s = scratch_address(st, &ws)) != MUON_OK) return s;
   muon::StepScalars sc{lr, mu, wd, scale, a, b, c, nesterov, ns_steps, 0};
-  return enqueue(plan->p, param_ptrs, grad_ptrs, mom_ptrs, sc, ws, st, false);
+  // no side stream: this entry point makes nothing, and its launches stay on `st`
+  return enqueue(nullptr, plan->p, param_ptrs, grad_ptrs, mom_ptrs, sc, ws, st, false);
 }
 
 muon_status muon_ns(muon_plan plan, const void* const* in_ptrs, float* const* out_ptrs,
@@ -445,7 +520,7 @@ muon_status muon_ns(muon_plan plan, const void* const* in_ptrs, float* const* ou
                                     workspace_bytes, &d);
   if (s != MUON_OK) return fail(s, d);
   muon::StepScalars sc{0.f, 0.f, 0.f, 1.f, a, b, c, 0, ns_steps, 1};
-  return enqueue(*P, (void* const*)out_ptrs, in_ptrs, nullptr, sc, workspace, (hipStream_t)stream);
+  return enqueue(plan, *P, (void* const*)out_ptrs, in_ptrs, nullptr, sc, workspace, (hipStream_t)stream);
 }
 
 muon_status muon_kernel_timing(int32_t enable) {

@@ -22,6 +22,10 @@ struct LargeArgs {
   bool whole;        // bf16 path: all NS steps in one group
   bool precise;      // bf16 path: split m x m chain with lo planes
   bool x0_lo;        // bf16 muon_step: X_0 carries its lo plane
+  // a second stream on the device with events that fork work onto it and
+  // join it back, or null (every launch on the launch stream)
+  hipStream_t side;
+  hipEvent_t ev_fork, ev_join;
 };
 
 // u32 indices, in the workspace's sync region, of the skinny path's timeout

@@ -41,8 +41,8 @@ TRAFFIC = {
            "fetch_kib_per_dispatch": 83727.4, "write_kib_per_dispatch": 109375.8,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
-           "kernel_source_sha256": "46e3f63396f0cba7517f653e5902ce362e1ab2faf2af81cc36f803bb104613cf",
-           "fetch_kib_per_dispatch": 12586613.7, "write_kib_per_dispatch": 1637869.7,
+           "kernel_source_sha256": "7793d6d3678bbc6d34639fad54bc75ee39f967ad914c031a0e7b3665bf677927",
+           "fetch_kib_per_dispatch": 13399637.3, "write_kib_per_dispatch": 1644755.0,
            "fetch_scale": 2.0, "write_scale": 1.0},
 }
 

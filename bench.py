@@ -41,7 +41,7 @@ TRAFFIC = {
            "fetch_kib_per_dispatch": 83727.4, "write_kib_per_dispatch": 109375.8,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
-           "kernel_source_sha256": "7793d6d3678bbc6d34639fad54bc75ee39f967ad914c031a0e7b3665bf677927",
+           "kernel_source_sha256": "7b5754a4467b5456382c56bf3fb943f65ff9246758579a8b4bd0b7754b158dc2",
            "fetch_kib_per_dispatch": 13399637.3, "write_kib_per_dispatch": 1644755.0,
            "fetch_scale": 2.0, "write_scale": 1.0},
 }

@@ -1339,25 +1339,35 @@ static hipError_t ns_group_bf16(const LargeArgs& g, hipStream_t st, int k, int G
   // later main-stream launch overwrites is P_0 (R_0 of R_1), by the poly of
   // step 2, which therefore waits for R_1.  The apply waits for the last R.
   const bool ovl = g.side && g.ev_fork && g.ev_join && up * g.count < g.cus * GemmGeom<TILE>::PER_CU;
-  bool joined = true;  // no R launch on the side stream that the launch stream has not waited for
+  // Work enqueued on the side stream that the launch stream has not waited
+  // for.  Every return after a fork joins first, errors included, so no R
+  // launch can still run beside what the caller enqueues next.
+  bool pend = false;
   auto join = [&]() -> hipError_t {
-    if (joined) return hipSuccess;
-    joined = true;
-    return hipStreamWaitEvent(st, g.ev_join, 0);
+    if (!pend) return hipSuccess;
+    pend = false;
+    const hipError_t e1 = hipEventRecord(g.ev_join, g.side);
+    const hipError_t e2 = hipStreamWaitEvent(st, g.ev_join, 0);
+    return e1 != hipSuccess ? e1 : e2;
+  };
+  auto bail = [&](hipError_t err) {
+    (void)join();
+    return err;
   };
   for (int j = 1; j < G; ++j) {
     const int pp = (j - 1) & 1;  // P_{j-1}
     // T = P A from A's planes into T's, A' = P T from T's planes into A's
     EpiSymMul et{H, Lo, Pdb[pp], Th, Tl, cs ? 1 : 0, mp};
-    if ((e = cs ? sym3(Pb[pp], PbL[pp], H, Lo, et) : sym1(Pb[pp], H, et)) != hipSuccess) return e;
+    if ((e = cs ? sym3(Pb[pp], PbL[pp], H, Lo, et) : sym1(Pb[pp], H, et)) != hipSuccess) return bail(e);
     EpiSymMul ea{Th, Tl, Pdb[pp], H, Lo, (split_a2(g.m, k + j, steps) || cs) ? 1 : 0, mp};
-    if ((e = cs ? sym3(Pb[pp], PbL[pp], Th, Tl, ea) : sym1(Pb[pp], Th, ea)) != hipSuccess) return e;
+    if ((e = cs ? sym3(Pb[pp], PbL[pp], Th, Tl, ea) : sym1(Pb[pp], Th, ea)) != hipSuccess) return bail(e);
     if (j == 2 && (e = join()) != hipSuccess) return e;  // R_1 has read P_0
-    if ((e = poly(j)) != hipSuccess) return e;
+    if ((e = poly(j)) != hipSuccess) return bail(e);
     hipStream_t rs = st;
     if (ovl) {
-      if ((e = hipEventRecord(g.ev_fork, st)) != hipSuccess) return e;
-      if ((e = hipStreamWaitEvent(g.side, g.ev_fork, 0)) != hipSuccess) return e;
+      if ((e = hipEventRecord(g.ev_fork, st)) != hipSuccess) return bail(e);
+      if ((e = hipStreamWaitEvent(g.side, g.ev_fork, 0)) != hipSuccess) return bail(e);
+      pend = true;
       rs = g.side;
     }
     auto sym1r = [&](const uint16_t* a, const uint16_t* b, const auto& epi) {
@@ -1382,11 +1392,7 @@ static hipError_t ns_group_bf16(const LargeArgs& g, hipStream_t st, int k, int G
                          (k == 0 && j == 1) ? 1 : 0, mp};
       e = sym1r(Pb[j & 1], r0, er);
     }
-    if (e != hipSuccess) return e;
-    if (ovl) {
-      if ((e = hipEventRecord(g.ev_join, g.side)) != hipSuccess) return e;
-      joined = false;
-    }
+    if (e != hipSuccess) return bail(e);
   }
   if ((e = join()) != hipSuccess) return e;
   // apply with R (P_0 for a single step): A = R (+ its lo plane, precise),

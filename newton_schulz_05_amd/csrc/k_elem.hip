@@ -17,6 +17,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace muon {
 
 namespace {
@@ -103,20 +105,33 @@ __global__ __launch_bounds__(kElemThreads) void adamw_kernel(AdamTable tab, Adam
   const bool vec = ((uintptr_t)p | (uintptr_t)g | (uintptr_t)m | (uintptr_t)v) % (VEC * sizeof(PT)) == 0 &&
                    ((uintptr_t)m | (uintptr_t)v) % 16 == 0 && base + kAdamChunk <= n;
   if (vec) {
+    constexpr int NI = int(kAdamChunk / (kElemThreads * VEC));
+    // every pass's loads are issued before the first store
+    typedef std::conditional_t<sizeof(PT) == 2, u32x2, f32x4> PW;
+    PW pwq[NI], gwq[NI];
+    f32x4 mvq[NI], vvq[NI];
 #pragma unroll
-    for (int i = 0; i < int(kAdamChunk / (kElemThreads * VEC)); ++i) {
+    for (int i = 0; i < NI; ++i) {
+      const int64_t e = base + (int64_t(i) * kElemThreads + threadIdx.x) * VEC;
+      mvq[i] = *(const f32x4*)(m + e);
+      vvq[i] = *(const f32x4*)(v + e);
+      pwq[i] = *(const PW*)(p + e);
+      gwq[i] = *(const PW*)(g + e);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
       const int64_t e = base + (int64_t(i) * kElemThreads + threadIdx.x) * VEC;
       float pv[VEC], gv[VEC];
-      f32x4 mv = *(const f32x4*)(m + e), vv = *(const f32x4*)(v + e);
+      f32x4 mv = mvq[i], vv = vvq[i];
       if constexpr (sizeof(PT) == 2) {
-        const u32x2 pw = *(const u32x2*)(p + e), gw = *(const u32x2*)(g + e);
+        const u32x2 pw = pwq[i], gw = gwq[i];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           pv[2 * j] = bf2f(uint16_t(pw[j] & 0xffffu)); pv[2 * j + 1] = bf2f(uint16_t(pw[j] >> 16));
           gv[2 * j] = bf2f(uint16_t(gw[j] & 0xffffu)); gv[2 * j + 1] = bf2f(uint16_t(gw[j] >> 16));
         }
       } else {
-        const f32x4 pw = *(const f32x4*)(p + e), gw = *(const f32x4*)(g + e);
+        const f32x4 pw = pwq[i], gw = gwq[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) { pv[j] = pw[j]; gv[j] = gw[j]; }
       }

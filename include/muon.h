@@ -114,8 +114,9 @@ typedef struct muon_plan_s* muon_plan;
 muon_status muon_plan_create(const muon_shape* shapes, int32_t n_params, muon_dtype param_dt,
                              muon_dtype grad_dt, muon_dtype mom_dt, muon_plan* out);
 
-/* Frees the plan, with its side streams and events (work still queued on a
- * side stream completes before they are released). */
+/* Frees the plan, with its side streams and events.  If the plan made a side
+ * stream, the host first waits for the work queued on it (launched by the
+ * plan's calls, which their streams wait for). */
 void muon_plan_destroy(muon_plan plan);
 
 /* Bytes of device workspace muon_step / muon_ns need for this plan. */

@@ -43,7 +43,9 @@ struct muon_plan_s {
       SideStream& ss = side[d];
       if (!ss.s && !ss.fork && !ss.join) continue;
       if (hipSetDevice(d) != hipSuccess) continue;
-      // work still queued on the stream completes before its resources go
+      // the host waits for the stream's queued work, so nothing still
+      // queued anywhere refers to the events when they go
+      if (ss.s) (void)hipStreamSynchronize(ss.s);
       if (ss.join) (void)hipEventDestroy(ss.join);
       if (ss.fork) (void)hipEventDestroy(ss.fork);
       if (ss.s) (void)hipStreamDestroy(ss.s);

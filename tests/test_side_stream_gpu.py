@@ -47,3 +47,28 @@ def test_side_stream_is_bitwise_neutral():
         for i, s in enumerate(SHAPES):
             assert torch.equal(a[i], b[i]), f"{name}[{i}] of {s} differs without the side stream"
             assert torch.equal(a[i], c[i]), f"{name}[{i}] of {s} differs between runs with it"
+
+
+def test_plan_destroyed_right_after_its_steps():
+    """Steps whose R launches went to the side stream, then the plan is
+    destroyed before anything is synchronised: the results must be those of
+    the same steps without the side stream (the destructor waits for the
+    side stream before it releases the stream and its events)."""
+    import gc
+    shapes = [(512, 1024)] * 4 + [(300, 700)] * 2
+    wl = WL.custom(shapes, g_std=1e-2, number=86)
+    ref = _steps(MuonPlan(wl.shapes, wl.dtype), wl, False)
+    plan = MuonPlan(wl.shapes, wl.dtype)
+    ws = plan.new_workspace(DEV)
+    params = WL.make_params(wl, DEV, "cpu")
+    moms = WL.make_moms(wl, DEV)
+    grads = [WL.make_grads(wl, s, DEV, "cpu") for s in range(3)]
+    torch.cuda.synchronize()
+    for s in range(3):
+        plan.step(params, grads[s], moms, **wl.hyper(), workspace=ws)
+    del plan
+    gc.collect()
+    torch.cuda.synchronize()
+    for i, s in enumerate(shapes):
+        assert torch.equal(params[i], ref[0][i]), f"W[{i}] of {s} differs"
+        assert torch.equal(moms[i], ref[1][i]), f"M[{i}] of {s} differs"

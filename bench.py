@@ -41,7 +41,7 @@ TRAFFIC = {
            "fetch_kib_per_dispatch": 83727.4, "write_kib_per_dispatch": 109375.8,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
-           "kernel_source_sha256": "7b5754a4467b5456382c56bf3fb943f65ff9246758579a8b4bd0b7754b158dc2",
+           "kernel_source_sha256": "e2aa5de95b016795d9304740bd8376cddffdd0471b56e19b9f34bfb3023351bc",
            "fetch_kib_per_dispatch": 13399637.3, "write_kib_per_dispatch": 1644755.0,
            "fetch_scale": 2.0, "write_scale": 1.0},
 }
@@ -236,7 +236,8 @@ def executed_flops(wl) -> float:
     the library's schedule: all NS steps in one group when m < 512, else the
     first min(4, N - 1), then pairs, then a single step; per group one Gram
     m^2 n, per step A^2 (one product m^3 in steps k < min(3, N - 2) when
-    m >= 512, else three), after the group's first step the products
+    m >= 1536, k < min(2, N - 2) when 512 <= m < 1536, else three), after
+    the group's first step the products
     T = P A, A' = P T and R = P R (m^3 each), and one apply 2 m^2 n.  The
     lo planes add products: the first Gram takes three (precise recipe,
     m < 4096 or more than 5 steps), the chain products three each (precise;
@@ -252,7 +253,8 @@ def executed_flops(wl) -> float:
             tot += b * (3.0 * m * m * n + m ** 3) * N
             continue
         whole, precise = m < 512, (m < 4096 or N > 5)
-        a2 = lambda k: (1 if (m >= 512 and k < min(3, N - 2)) else 3) * m ** 3  # noqa: E731
+        plain = 3 if m >= 1536 else 2
+        a2 = lambda k: (1 if (m >= 512 and k < min(plain, N - 2)) else 3) * m ** 3  # noqa: E731
         chain = 3 if precise else 1
         rprod = 1 if (not precise or (m >= 1024 and N <= 5)) else 3
         f, k = 0.0, 0

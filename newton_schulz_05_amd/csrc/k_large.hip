@@ -1230,9 +1230,10 @@ static hipError_t gemm_launch(const uint16_t* Ah, const uint16_t* Al, int64_t ld
 }
 
 // A^2 takes the single product H H in the first NS steps and the split-bf16
-// products (H H + H L + L H, about 16 mantissa bits of A) after them: for
-// m >= kPlainMinM the single product is taken in steps k < min(kPlainSteps,
-// ns_steps - 2), for smaller m never.  NS pulls every singular value towards
+// products (H H + H L + L H, about 16 mantissa bits of A) after them: the
+// single product is taken in steps k < min(kPlainSteps, ns_steps - 2) for
+// m >= kPlain3FromM, in steps k < min(kPlainStepsMid, ns_steps - 2) for
+// kPlainMinM <= m < kPlain3FromM, and never for smaller m.  NS pulls every singular value towards
 // its fixed band and damps a perturbation of P on the way there; once the
 // bulk of the normalised singular values (about 1/sqrt(m) at the start, times
 // up to a = 3.4445 per step) has reached the band, the rounding of A shows in
@@ -1243,12 +1244,22 @@ static hipError_t gemm_launch(const uint16_t* Ah, const uint16_t* Al, int64_t ld
 // inputs with singular values spread over 1e-1 .. 1e-4 the same), while a
 // single product in step 3 (of 5 or 6) or in the last step raised it by
 // 15-240%; at m = 33 .. 130 step 2 already counts (5.6e-3 -> 8.4e-3 at
-// 130 x 200).
+// 130 x 200).  Inputs of low rank or with spectra over three decades, in
+// the grouped precise recipe, need step 2 split below m = 1536: emulated
+// (and on the GPU to three digits) for 5 steps, rank m/8 gave 3.4e-2 with
+// a single product in step 2 against 6.5e-3 split at 512 x 1024, 1.5e-2
+// against 6.0e-3 at 768 x 1024, 9.5e-3 against 6.4e-3 at 1024^2, 7.4e-3
+// against 6.0e-3 at 1280 x 2048, 6.5e-3 against 5.8e-3 at 1536 x 2048; and
+// singular values log-spaced over [1e-3, 1] 1.0e-2 against 3.5e-3 at
+// 512 x 1024.
 constexpr int kPlainSteps = 3;
+constexpr int kPlainStepsMid = 2;
 constexpr int64_t kPlainMinM = 512;
+constexpr int64_t kPlain3FromM = 1536;
 
 static inline bool split_a2(int64_t m, int k, int steps) {
-  return m < kPlainMinM || k >= std::min(kPlainSteps, steps - 2);
+  if (m < kPlainMinM) return true;
+  return k >= std::min(m >= kPlain3FromM ? kPlainSteps : kPlainStepsMid, steps - 2);
 }
 
 // A group of G >= 1 consecutive NS steps k .. k+G-1 of the bf16 path, with

@@ -40,9 +40,10 @@ def test_executed_count_grouped_steps_on_the_large_pair():
 def test_executed_count_group_lengths(ns_steps, groups):
     # precise recipe (512 <= m < 4096): first Gram with X_0's lo plane (3
     # products), chain products split (3 each), applies with R's lo plane and,
-    # in the first group, X_0's
+    # in the first group, X_0's; below m = 1536 A^2 is a single product in
+    # steps 0-1 only
     m, n = 600, 1300
-    split = [k >= min(3, ns_steps - 2) for k in range(ns_steps)]
+    split = [k >= min(2, ns_steps - 2) for k in range(ns_steps)]
     want, k = 0, 0
     for g in groups:
         gram = (3 if k == 0 else 1) * m * m * n

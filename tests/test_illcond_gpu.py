@@ -4,7 +4,9 @@ spread over decades, unlike the Gaussian inputs of the workloads.  Inputs:
 singular values log-spaced over [1e-2, 1] and [1e-3, 1], and rank-m/8
 products, at the shapes of the workloads' groups: the experts [2048, 1536]
 (stored tall), the transformer's [4096, 4096] and [4096, 14336], and the
-skinny [24, 10240].
+skinny [24, 10240]; and at [512, 1024] and [1024, 1024], where the precise
+recipe's A^2 must be split from step 2 on (a single product there gave
+3.4e-2 on the rank-m/8 input at 512 x 1024).
 
 Both entry points are compared with the fp64 oracle at the bf16 bars
 (max-abs 3e-2, relative Frobenius 1e-2):
@@ -28,7 +30,7 @@ from tests.helpers import check_o, host64
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 QUINTIC = (3.4445, -4.7750, 2.0315)
-SHAPES = [(2048, 1536), (4096, 4096), (4096, 14336), (24, 10240)]
+SHAPES = [(2048, 1536), (4096, 4096), (4096, 14336), (24, 10240), (512, 1024), (1024, 1024)]
 KINDS = ["log2", "log3", "rank8"]
 
 

@@ -37,8 +37,8 @@ F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 # was taken on (SHA-256); otherwise `traffic` is reported as null.
 TRAFFIC = {
     "c2": {"source": "k_skinny.hip",
-           "kernel_source_sha256": "de1e80a431de6622585be7aa758452062d9b18ccfca13aafbfe7406fd5fe82f5",
-           "fetch_kib_per_dispatch": 83727.4, "write_kib_per_dispatch": 109375.8,
+           "kernel_source_sha256": "cac0cc5772ca9aef843768a8960ccd6aab896dbd0a6389517a65d061a7ccc6d0",
+           "fetch_kib_per_dispatch": 83702.2, "write_kib_per_dispatch": 110722.4,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
            "kernel_source_sha256": "e2aa5de95b016795d9304740bd8376cddffdd0471b56e19b9f34bfb3023351bc",

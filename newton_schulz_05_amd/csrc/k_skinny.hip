@@ -321,23 +321,42 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
     return (r < m) ? uint32_t(r * nn + c0 + (v * kNB + q) * 32 + 16 * hc) : kOob;
   };
   u32x4 pg[2][2], pm[2][4];  // prefetched G and M of a block (ping-pong by block parity)
-  // Gram contribution of one block: stage the block column-major in this
-  // wave's LDS area, read it back row-per-lane, one MFMA per 16 columns.
-  // Taken per block inside the momentum loop, while the next block's loads
-  // are in flight.
-  // With the lo part xl (muon_step), X0 X0^T ~ Xh Xh^T + Xh Xl^T + Xl Xh^T,
-  // taken in that order per 16 columns.
-  auto gram_block = [&](const uint32_t* x, f32x16& gacc, int lane) {
+  // The Gram of X0, block by block inside the momentum loop while the next
+  // block's loads are in flight: with the block staged column-major in this
+  // wave's LDS area ([column][row], bf16), a lane reads row (lane % 32),
+  // 8 columns per 16-column half, which is both the A and the B fragment of
+  // the block's MFMA (one per 16 columns).
+  // In muon_step U's lo part enters too, X0 X0^T ~ Xh Xh^T + Xh Xl^T +
+  // Xl Xh^T, taken in that order per 16 columns, with lo = bf16(U - hi)
+  // staged the same way (U to about 2^-16, like the codes the apply
+  // decodes).  On rank-3 inputs [24, 10240] the relative Frobenius error of
+  // the step's O was 1.06e-2 to 1.20e-2 with Xh Xh^T alone (GPU, two seeds)
+  // and 3.5e-3 to 3.8e-3 with the lo products.
+  auto gram_frag = [&](int tt, int lane) {
+    const int h = lane >> 5, cl = lane & 31;
+    u16x8 f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = stg[(16 * tt + 8 * h + e) * kLdr + cl];
+    return as_bf16x8(f);
+  };
+  auto gram_frags = [&](bf16x8* f2, int lane) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) f2[tt] = gram_frag(tt, lane);
+  };
+  // stage a block held in the register layout (x: bf16 pairs) column-major
+  auto stage_reg = [&](const uint32_t* x, int lane) {
     const int h = lane >> 5, cl = lane & 31;
 #pragma unroll
     for (int g = 0; g < 4; ++g) *(u32x2*)(stg + cl * kLdr + 8 * g + 4 * h) = u32x2{x[2 * g], x[2 * g + 1]};
+  };
+  auto gram_mfma = [&](const bf16x8* fb, const bf16x8* fl, f32x16& gacc) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      u16x8 f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = stg[(16 * tt + 8 * h + e) * kLdr + cl];
-      const bf16x8 fb = as_bf16x8(f);
-      gacc = mfma32x32x16(fb, fb, gacc);
+      gacc = mfma32x32x16(fb[tt], fb[tt], gacc);
+      if constexpr (step_mode) {
+        gacc = mfma32x32x16(fb[tt], fl[tt], gacc);
+        gacc = mfma32x32x16(fl[tt], fb[tt], gacc);
+      }
     }
   };
 
@@ -385,12 +404,33 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
         for (int i = 0; i < 4; ++i) buf_st_b128(rM, e0 * 4 + 16 * i, pm[q & 1][i]);
       }
       // stage column-major [col][row] (bf16), then read the register layout
+      // and the Gram's fragments
 #pragma unroll
       for (int j = 0; j < 16; ++j) stg[(16 * hc + j) * kLdr + r] = f2bf(u[j]);
       __builtin_amdgcn_wave_barrier();
+      // with m <= 24 (KS 6) dwords 6 and 7 hold rows 24-31, padding: zeros
+      // known to the compiler, so they hold no registers
 #pragma unroll
-      for (int d = 0; d < 8; ++d) xw[q][d] = *(const uint32_t*)(stg + cl * kLdr + row_of(2 * d, h));
+      for (int d = 0; d < 8; ++d)
+        xw[q][d] = (KS == 6 && d >= 6) ? 0u : *(const uint32_t*)(stg + cl * kLdr + row_of(2 * d, h));
+      bf16x8 fb[2];
+      gram_frags(fb, lane);
       __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) gacc = mfma32x32x16(fb[tt], fb[tt], gacc);
+      if constexpr (step_mode) {
+        // lo staged over hi; one lo fragment at a time (register pressure)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) stg[(16 * hc + j) * kLdr + r] = f2bf(u[j] - bf2f(f2bf(u[j])));
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const bf16x8 fl = gram_frag(tt, lane);
+          gacc = mfma32x32x16(fb[tt], fl, gacc);
+          gacc = mfma32x32x16(fl, fb[tt], gacc);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
       if (step_mode) {
         // each code goes straight to its place in the register layout:
         // row r is value 4 (r / 8) + r % 4 of lane 32 ((r / 4) % 2) + column
@@ -438,7 +478,25 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
         uu[r] = u;
       }
 #pragma unroll
-      for (int d = 0; d < 8; ++d) xw[q][d] = f2bf2(uu[2 * d], uu[2 * d + 1]);
+      for (int d = 0; d < 8; ++d) xw[q][d] = (KS == 6 && d >= 6) ? 0u : f2bf2(uu[2 * d], uu[2 * d + 1]);
+      bf16x8 fb[2], fl[2];
+      stage_reg(xw[q], lane);
+      __builtin_amdgcn_wave_barrier();
+      gram_frags(fb, lane);
+      if constexpr (step_mode) {
+        uint32_t xl[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+          xl[d] = (KS == 6 && d >= 6) ? 0u
+                                      : f2bf2(uu[2 * d] - bf2f(uint16_t(xw[q][d] & 0xffffu)),
+                                              uu[2 * d + 1] - bf2f(uint16_t(xw[q][d] >> 16)));
+        __builtin_amdgcn_wave_barrier();
+        stage_reg(xl, lane);
+        __builtin_amdgcn_wave_barrier();
+        gram_frags(fl, lane);
+      }
+      __builtin_amdgcn_wave_barrier();
+      gram_mfma(fb, fl, gacc);
       if (step_mode) {
         uint32_t code[4];
         lo_codes(uu, xw[q], code);
@@ -451,7 +509,6 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    gram_block(xw[q], gacc, opaque(int(threadIdx.x)) & 63);
   }
 
   // ---- helpers ---------------------------------------------------------------

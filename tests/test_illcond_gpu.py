@@ -54,3 +54,22 @@ def test_ill_conditioned_input(shape, kind):
     assert np.array_equal(host64(mom), host64(g_cpu))  # M = 0.95 * 0 + G
     print(f"[illcond] {shape} {kind}: ns relF {r_ns:.2e} maxabs {a_ns:.1e}; "
           f"step relF {r_st:.2e} maxabs {a_st:.1e}", flush=True)
+
+
+@pytest.mark.parametrize("seed", [7101, 7202])
+@pytest.mark.parametrize("shape", [(24, 10240), (28, 10240)], ids=["24x10240", "28x10240"])
+def test_skinny_low_rank_step(shape, seed):
+    """The skinny step on rank-m/8 inputs, at seeds where U's lo part taken
+    in the apply only left the step's O at 1.06e-2 to 1.27e-2 (above the
+    bar): with lo in the Gram as well it is 2.7e-3 to 3.9e-3."""
+    print(f"[illcond] skinny {shape} rank8 seed {seed}", flush=True)
+    g_cpu = WL.spectral(*shape, "rank8", seed)
+    g = g_cpu.to(DEV)
+    plan = MuonPlan([shape], torch.bfloat16)
+    w = torch.zeros(shape, dtype=torch.bfloat16, device=DEV)
+    mom = torch.zeros(shape, dtype=torch.float32, device=DEV)
+    plan.step([w], [g], [mom], lr=-1.0, mu=0.95, nesterov=True, wd=0.0)
+    torch.cuda.synchronize()
+    o_ref = ref.newton_schulz(1.95 * host64(g_cpu), *QUINTIC, 5)
+    r_st, a_st = check_o(host64(w), o_ref, True, f"step O {shape} rank8 seed {seed}")
+    print(f"[illcond] skinny {shape} rank8 seed {seed}: step relF {r_st:.2e} maxabs {a_st:.1e}", flush=True)

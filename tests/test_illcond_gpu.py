@@ -73,3 +73,26 @@ def test_skinny_low_rank_step(shape, seed):
     o_ref = ref.newton_schulz(1.95 * host64(g_cpu), *QUINTIC, 5)
     r_st, a_st = check_o(host64(w), o_ref, True, f"step O {shape} rank8 seed {seed}")
     print(f"[illcond] skinny {shape} rank8 seed {seed}: step relF {r_st:.2e} maxabs {a_st:.1e}", flush=True)
+
+
+SMALL = [(33, 132), (64, 64), (200, 100), (448, 1792), (640, 2560)]
+
+
+@pytest.mark.parametrize("kind", ["rank8", "log3"])
+@pytest.mark.parametrize("shape", SMALL, ids=[f"{r}x{c}" for r, c in SMALL])
+def test_ill_conditioned_small_and_mid_shapes(shape, kind):
+    """The whole recipe (m < 512, one group of all steps) and the precise
+    recipe below the A^2 cutoff, on the same kinds of input, muon_step's O
+    against the oracle at the same bars."""
+    seed = 9100 + 10 * SMALL.index(shape) + (0 if kind == "rank8" else 1)
+    print(f"[illcond] {shape} {kind} seed {seed}", flush=True)
+    g_cpu = WL.spectral(*shape, kind, seed)
+    g = g_cpu.to(DEV)
+    plan = MuonPlan([shape], torch.bfloat16)
+    w = torch.zeros(shape, dtype=torch.bfloat16, device=DEV)
+    mom = torch.zeros(shape, dtype=torch.float32, device=DEV)
+    plan.step([w], [g], [mom], lr=-1.0, mu=0.95, nesterov=True, wd=0.0)
+    torch.cuda.synchronize()
+    o_ref = ref.newton_schulz(1.95 * host64(g_cpu), *QUINTIC, 5)
+    r_st, a_st = check_o(host64(w), o_ref, True, f"step O {shape} {kind}")
+    print(f"[illcond] {shape} {kind}: step relF {r_st:.2e} maxabs {a_st:.1e}", flush=True)

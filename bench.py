@@ -37,12 +37,12 @@ F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 # was taken on (SHA-256); otherwise `traffic` is reported as null.
 TRAFFIC = {
     "c2": {"source": "k_skinny.hip",
-           "kernel_source_sha256": "cac0cc5772ca9aef843768a8960ccd6aab896dbd0a6389517a65d061a7ccc6d0",
-           "fetch_kib_per_dispatch": 83702.2, "write_kib_per_dispatch": 110722.4,
+           "kernel_source_sha256": "ddf6e8a005d0db348679e46b7733db2503b93c4d6f16870ce9d228aae708215e",
+           "fetch_kib_per_dispatch": 84689.6, "write_kib_per_dispatch": 113664.5,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
            "kernel_source_sha256": "e2aa5de95b016795d9304740bd8376cddffdd0471b56e19b9f34bfb3023351bc",
-           "fetch_kib_per_dispatch": 13100890.1, "write_kib_per_dispatch": 1640979.0,
+           "fetch_kib_per_dispatch": 13327763.5, "write_kib_per_dispatch": 1645024.6,
            "fetch_scale": 2.0, "write_scale": 1.0},
 }
 

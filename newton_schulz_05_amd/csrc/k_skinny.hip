@@ -326,12 +326,17 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   // wave's LDS area ([column][row], bf16), a lane reads row (lane % 32),
   // 8 columns per 16-column half, which is both the A and the B fragment of
   // the block's MFMA (one per 16 columns).
-  // In muon_step U's lo part enters too, X0 X0^T ~ Xh Xh^T + Xh Xl^T +
-  // Xl Xh^T, taken in that order per 16 columns, with lo = bf16(U - hi)
-  // staged the same way (U to about 2^-16, like the codes the apply
-  // decodes).  On rank-3 inputs [24, 10240] the relative Frobenius error of
-  // the step's O was 1.06e-2 to 1.20e-2 with Xh Xh^T alone (GPU, two seeds)
-  // and 3.5e-3 to 3.8e-3 with the lo products.
+  // In muon_step U's lo part enters too, X0 X0^T = (Xh + Xl)(Xh + Xl)^T =
+  // Xh Xh^T + Xh Xl^T + Xl Xh^T + Xl Xl^T, taken in that order per 16
+  // columns, with lo = bf16(U - hi) staged the same way (U to about 2^-16,
+  // like the codes the apply decodes).  On rank-3 inputs [24, 10240] the
+  // relative Frobenius error of the step's O was 1.06e-2 to 1.20e-2 with
+  // Xh Xh^T alone (GPU, two seeds) and 3.5e-3 to 3.8e-3 with the lo
+  // products.  Xl Xl^T, though of relative size 2^-18, keeps A0 a Gram
+  // matrix: without it A0 lacks a positive semidefinite term and has
+  // negative eigenvalues of about that size where U has none (low rank),
+  // which the NS recurrence multiplies by about a^2 per step (a rank-3
+  // input went to NaN in 10 steps).
   auto gram_frag = [&](int tt, int lane) {
     const int h = lane >> 5, cl = lane & 31;
     u16x8 f;
@@ -356,6 +361,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       if constexpr (step_mode) {
         gacc = mfma32x32x16(fb[tt], fl[tt], gacc);
         gacc = mfma32x32x16(fl[tt], fb[tt], gacc);
+        gacc = mfma32x32x16(fl[tt], fl[tt], gacc);
       }
     }
   };
@@ -428,6 +434,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
           const bf16x8 fl = gram_frag(tt, lane);
           gacc = mfma32x32x16(fb[tt], fl, gacc);
           gacc = mfma32x32x16(fl, fb[tt], gacc);
+          gacc = mfma32x32x16(fl, fl, gacc);
         }
         __builtin_amdgcn_wave_barrier();
       }

@@ -21,7 +21,8 @@
  * How the NS iteration is evaluated (the result is that iteration's, up to
  * rounding):
  *   - bf16, min(M, N) <= 32: X = Q_k X0 with Q_k a polynomial in X0 X0^T,
- *     run in fp32 on the small m x m matrices (one Gram of X0 per call);
+ *     run in fp32 on the small m x m matrices (one Gram of X0 per call; in
+ *     muon_step X0 = U as a bf16 hi and lo pair, in the Gram and the apply);
  *   - bf16, larger: X stored in bf16, products on bf16 MFMA with fp32
  *     accumulation.  U enters as a bf16 hi and lo pair (muon_step).  The
  *     steps run in groups (the first min(ns_steps, 5) when min(M, N) < 512,
@@ -30,7 +31,8 @@
  *     in the m x m space (A_{k+1} = P_k A_k P_k, R = P_last ... P_first).
  *     Below min(M, N) = 4096, or beyond 5 steps, the m x m products take
  *     split-bf16 operands (about 16 mantissa bits); A^2 is split except in
- *     the first min(3, ns_steps - 2) steps when min(M, N) >= 512;
+ *     the first min(3, ns_steps - 2) steps when min(M, N) >= 1536 and the
+ *     first min(2, ns_steps - 2) when 512 <= min(M, N) < 1536;
  *   - fp32: the same sequence as the bf16 path for larger matrices but with
  *     fp32 FMA arithmetic throughout, one step at a time.
  * The bf16 O is within 1e-2 relative Frobenius (3e-2 max-abs) of the exact
@@ -141,7 +143,12 @@ muon_status muon_plan_group_info(muon_plan plan, int32_t g, int64_t* m, int64_t*
  *   lr, wd, scale, mu : finite; mu in [0, 1); nesterov 0 or 1.
  *   a, b, c    : NS polynomial coefficients, finite.
  *   ns_steps   : 0 .. 16 (the accuracy stated above is measured for the
- *                workloads' 5 steps; it is checked on the GPU up to 16).
+ *                workloads' 5 steps; on Gaussian inputs it is checked on the
+ *                GPU up to 16.  Beyond 5 steps NS carries an input's near-null
+ *                directions, such as the bf16 rounding of a low-rank matrix,
+ *                into its band, and bf16 arithmetic cannot follow them: on
+ *                rank min(M, N) / 8 inputs O is then 2e-2 to 2e-1 from the
+ *                exact iteration).
  *   workspace  : device buffer of at least muon_plan_workspace_bytes(),
  *                256-byte aligned, zero-filled once before first use.
  * Tensor results do not depend on how matrices are grouped or batched:

@@ -147,8 +147,8 @@ muon_status muon_plan_group_info(muon_plan plan, int32_t g, int64_t* m, int64_t*
  *                GPU up to 16.  Beyond 5 steps NS carries an input's near-null
  *                directions, such as the bf16 rounding of a low-rank matrix,
  *                into its band, and bf16 arithmetic cannot follow them: on
- *                rank min(M, N) / 8 inputs O is then 2e-2 to 2e-1 from the
- *                exact iteration).
+ *                rank min(M, N) / 8 inputs O is then 2e-2 to 3e-1 from the
+ *                exact iteration, finite and bounded up to 16 steps).
  *   workspace  : device buffer of at least muon_plan_workspace_bytes(),
  *                256-byte aligned, zero-filled once before first use.
  * Tensor results do not depend on how matrices are grouped or batched:

@@ -37,7 +37,7 @@ F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 # was taken on (SHA-256); otherwise `traffic` is reported as null.
 TRAFFIC = {
     "c2": {"source": "k_skinny.hip",
-           "kernel_source_sha256": "ddf6e8a005d0db348679e46b7733db2503b93c4d6f16870ce9d228aae708215e",
+           "kernel_source_sha256": "2f1fe8242878c4e6f71fc19283f621f5324ad83951c6bf361292173e1254192d",
            "fetch_kib_per_dispatch": 84689.6, "write_kib_per_dispatch": 113664.5,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",

@@ -20,10 +20,11 @@
 // rounding of an iterate), which is also more accurate than iterating on a
 // bf16 X.
 //
-// Arithmetic: X0 is held in bf16; the Gram uses bf16 MFMA with fp32
-// accumulation (exact products); Q_K is split into bf16 hi + lo parts so the
-// apply is accurate to about 16 mantissa bits of Q_K; O stays fp32 up to the
-// weight update.
+// Arithmetic: X0 is held in bf16 (in muon_step as U's hi part, with its lo
+// part as 8-bit codes); the Gram uses bf16 MFMA with fp32 accumulation
+// (exact products), of hi + lo in muon_step; Q_K is split into bf16 hi + lo
+// parts so the apply is accurate to about 16 mantissa bits of Q_K, and adds
+// Q_hi times X0's lo part; O stays fp32 up to the weight update.
 //
 // Register layout (wave64, MFMA 32x32x16): a "block" is 32 columns of the
 // slab.  Lane l (h = l / 32, c = l % 32) holds column c of the block at the

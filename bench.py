@@ -37,8 +37,8 @@ F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 # was taken on (SHA-256); otherwise `traffic` is reported as null.
 TRAFFIC = {
     "c2": {"source": "k_skinny.hip",
-           "kernel_source_sha256": "2f1fe8242878c4e6f71fc19283f621f5324ad83951c6bf361292173e1254192d",
-           "fetch_kib_per_dispatch": 84689.6, "write_kib_per_dispatch": 113664.5,
+           "kernel_source_sha256": "796b541d06824e8f9e90d78bc7766427de5179477045250cafd652638197f4f9",
+           "fetch_kib_per_dispatch": 83623.0, "write_kib_per_dispatch": 110721.2,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
            "kernel_source_sha256": "e2aa5de95b016795d9304740bd8376cddffdd0471b56e19b9f34bfb3023351bc",

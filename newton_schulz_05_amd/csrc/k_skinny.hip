@@ -328,12 +328,13 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   // 8 columns per 16-column half, which is both the A and the B fragment of
   // the block's MFMA (one per 16 columns).
   // In muon_step U's lo part enters too, X0 X0^T = (Xh + Xl)(Xh + Xl)^T =
-  // Xh Xh^T + Xh Xl^T + Xl Xh^T + Xl Xl^T, taken in that order per 16
-  // columns, with lo = bf16(U - hi) staged the same way (U to about 2^-16,
-  // like the codes the apply decodes).  On rank-3 inputs [24, 10240] the
-  // relative Frobenius error of the step's O was 1.06e-2 to 1.20e-2 with
-  // Xh Xh^T alone (GPU, two seeds) and 3.5e-3 to 3.8e-3 with the lo
-  // products.  Xl Xl^T, though of relative size 2^-18, keeps A0 a Gram
+  // Xh Xh^T + Xh Xl^T + Xl Xh^T + Xl Xl^T: per block Xh Xh^T over its 32
+  // columns, then the lo products per 16 columns in that order, with
+  // lo = bf16(U - hi) staged over hi (U to about 2^-16, like the codes the
+  // apply decodes) and one lo fragment held at a time (register pressure).
+  // On rank-3 inputs [24, 10240] the relative Frobenius error of the step's
+  // O was 1.06e-2 to 1.20e-2 with Xh Xh^T alone (GPU, two seeds) and about
+  // 2.6e-3 with the lo products.  Xl Xl^T, though of relative size 2^-18, keeps A0 a Gram
   // matrix: without it A0 lacks a positive semidefinite term and has
   // negative eigenvalues of about that size where U has none (low rank),
   // which the NS recurrence multiplies by about a^2 per step (a rank-3
@@ -354,17 +355,6 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
     const int h = lane >> 5, cl = lane & 31;
 #pragma unroll
     for (int g = 0; g < 4; ++g) *(u32x2*)(stg + cl * kLdr + 8 * g + 4 * h) = u32x2{x[2 * g], x[2 * g + 1]};
-  };
-  auto gram_mfma = [&](const bf16x8* fb, const bf16x8* fl, f32x16& gacc) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      gacc = mfma32x32x16(fb[tt], fb[tt], gacc);
-      if constexpr (step_mode) {
-        gacc = mfma32x32x16(fb[tt], fl[tt], gacc);
-        gacc = mfma32x32x16(fl[tt], fb[tt], gacc);
-        gacc = mfma32x32x16(fl[tt], fl[tt], gacc);
-      }
-    }
   };
 
   f32x16 gacc = f32x16{};
@@ -487,10 +477,13 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       }
 #pragma unroll
       for (int d = 0; d < 8; ++d) xw[q][d] = (KS == 6 && d >= 6) ? 0u : f2bf2(uu[2 * d], uu[2 * d + 1]);
-      bf16x8 fb[2], fl[2];
+      bf16x8 fb[2];
       stage_reg(xw[q], lane);
       __builtin_amdgcn_wave_barrier();
       gram_frags(fb, lane);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) gacc = mfma32x32x16(fb[tt], fb[tt], gacc);
       if constexpr (step_mode) {
         uint32_t xl[8];
 #pragma unroll
@@ -498,13 +491,17 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
           xl[d] = (KS == 6 && d >= 6) ? 0u
                                       : f2bf2(uu[2 * d] - bf2f(uint16_t(xw[q][d] & 0xffffu)),
                                               uu[2 * d + 1] - bf2f(uint16_t(xw[q][d] >> 16)));
-        __builtin_amdgcn_wave_barrier();
         stage_reg(xl, lane);
         __builtin_amdgcn_wave_barrier();
-        gram_frags(fl, lane);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const bf16x8 fl = gram_frag(tt, lane);
+          gacc = mfma32x32x16(fb[tt], fl, gacc);
+          gacc = mfma32x32x16(fl, fb[tt], gacc);
+          gacc = mfma32x32x16(fl, fl, gacc);
+        }
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_wave_barrier();
-      gram_mfma(fb, fl, gacc);
       if (step_mode) {
         uint32_t code[4];
         lo_codes(uu, xw[q], code);

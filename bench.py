@@ -42,7 +42,7 @@ TRAFFIC = {
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
            "kernel_source_sha256": "e2aa5de95b016795d9304740bd8376cddffdd0471b56e19b9f34bfb3023351bc",
-           "fetch_kib_per_dispatch": 13327763.5, "write_kib_per_dispatch": 1645024.6,
+           "fetch_kib_per_dispatch": 13371509.1, "write_kib_per_dispatch": 1644963.9,
            "fetch_scale": 2.0, "write_scale": 1.0},
 }
 

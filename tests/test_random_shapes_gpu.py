@@ -35,8 +35,9 @@ def _random_set(seed):
 
 
 def _random_large_set(seed):
-    """m in [512, 1100] and n in [m, 3m]: single steps with the single-product
-    A^2 of the first steps when n < 2m, grouped steps when n >= 2m."""
+    """m in [512, 1100] and n in [m, 3m]: grouped steps (4 + 1) of the precise
+    recipe, with the single-product A^2 of the first steps (two below
+    m = 1536)."""
     rng = random.Random(seed)
     shapes = []
     for _ in range(rng.randint(1, 3)):

@@ -37,7 +37,7 @@ F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 # was taken on (SHA-256); otherwise `traffic` is reported as null.
 TRAFFIC = {
     "c2": {"source": "k_skinny.hip",
-           "kernel_source_sha256": "796b541d06824e8f9e90d78bc7766427de5179477045250cafd652638197f4f9",
+           "kernel_source_sha256": "8b2be37d3aa02cf54bcfaca3aeb148eda16a0650621c53c9d0b3ee0a2df5e6f2",
            "fetch_kib_per_dispatch": 83623.0, "write_kib_per_dispatch": 110721.2,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",

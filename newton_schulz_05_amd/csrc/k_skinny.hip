@@ -313,7 +313,9 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   // (r = lane / 2, half = lane % 2) moves 16 consecutive columns of row r with
   // 16-byte accesses, and the block is transposed to the register layout
   // through this wave's LDS staging.  The next block's loads are issued before
-  // the current block is processed.  Other blocks use element accesses.
+  // the current block is processed (m <= 24) or after its hi Gram (m > 24,
+  // whose larger register slab left the prefetch spilling: 76 -> 56 bytes of
+  // spill, 74 x [32, 10240] 5% faster).  Other blocks use element accesses.
   const bool vec = !tr && (nn % 8) == 0;
   uint16_t* stg = sh.stage[v];
   auto full = [&](int q) { return vec && c0 + (v * kNB + q) * 32 + 32 <= c1; };
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   if (full(0)) issue(0);
 #pragma unroll
   for (int q = 0; q < kNB; ++q) {
-    if (q + 1 < kNB && full(q + 1)) issue(q + 1);
+    if (KS == 6 && q + 1 < kNB && full(q + 1)) issue(q + 1);
     const int lane = opaque(int(threadIdx.x)) & 63, h = lane >> 5, cl = lane & 31;
     if (full(q)) {
       const int r = lane >> 1, hc = lane & 1;
@@ -415,6 +417,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) gacc = mfma32x32x16(fb[tt], fb[tt], gacc);
+      if (KS != 6 && q + 1 < kNB && full(q + 1)) issue(q + 1);
       if constexpr (step_mode) {
         // lo staged over hi; one lo fragment at a time (register pressure)
 #pragma unroll

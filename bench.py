@@ -37,8 +37,8 @@ F32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 # was taken on (SHA-256); otherwise `traffic` is reported as null.
 TRAFFIC = {
     "c2": {"source": "k_skinny.hip",
-           "kernel_source_sha256": "8b2be37d3aa02cf54bcfaca3aeb148eda16a0650621c53c9d0b3ee0a2df5e6f2",
-           "fetch_kib_per_dispatch": 83623.0, "write_kib_per_dispatch": 110721.2,
+           "kernel_source_sha256": "cefd602ce9e54d7d2fd93a486544604e79077dc96bbe74c5fb159af64c6d75cd",
+           "fetch_kib_per_dispatch": 83655.9, "write_kib_per_dispatch": 108731.0,
            "fetch_scale": 2.0, "write_scale": 1.0},
     "c5": {"source": "k_large.hip",
            "kernel_source_sha256": "e2aa5de95b016795d9304740bd8376cddffdd0471b56e19b9f34bfb3023351bc",

@@ -312,10 +312,12 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   // Wide matrices with 16-byte aligned rows take the vector path: lane
   // (r = lane / 2, half = lane % 2) moves 16 consecutive columns of row r with
   // 16-byte accesses, and the block is transposed to the register layout
-  // through this wave's LDS staging.  The next block's loads are issued before
-  // the current block is processed (m <= 24) or after its hi Gram (m > 24,
-  // whose larger register slab left the prefetch spilling: 76 -> 56 bytes of
-  // spill, 74 x [32, 10240] 5% faster).  Other blocks use element accesses.
+  // through this wave's LDS staging.  The next block's loads are issued once
+  // the current block's hi Gram (m <= 24) or all its Gram products (m > 24)
+  // are issued: earlier, the prefetch registers live across the block's
+  // arithmetic made the kernel spill (m <= 24: 16 -> 0 bytes, C2 1% faster;
+  // m > 24: 76 -> 40 bytes, 74 x [32, 10240] 10% faster).  Other blocks use
+  // element accesses.
   const bool vec = !tr && (nn % 8) == 0;
   uint16_t* stg = sh.stage[v];
   auto full = [&](int q) { return vec && c0 + (v * kNB + q) * 32 + 32 <= c1; };
@@ -376,7 +378,6 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
   if (full(0)) issue(0);
 #pragma unroll
   for (int q = 0; q < kNB; ++q) {
-    if (KS == 6 && q + 1 < kNB && full(q + 1)) issue(q + 1);
     const int lane = opaque(int(threadIdx.x)) & 63, h = lane >> 5, cl = lane & 31;
     if (full(q)) {
       const int r = lane >> 1, hc = lane & 1;
@@ -417,7 +418,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) gacc = mfma32x32x16(fb[tt], fb[tt], gacc);
-      if (KS != 6 && q + 1 < kNB && full(q + 1)) issue(q + 1);
+      if (KS == 6 && q + 1 < kNB && full(q + 1)) issue(q + 1);
       if constexpr (step_mode) {
         // lo staged over hi; one lo fragment at a time (register pressure)
 #pragma unroll
@@ -432,6 +433,7 @@ __global__ __launch_bounds__(256, 3) void skinny_kernel(MatTable tab, StepScalar
         }
         __builtin_amdgcn_wave_barrier();
       }
+      if (KS != 6 && q + 1 < kNB && full(q + 1)) issue(q + 1);
       if (step_mode) {
         // each code goes straight to its place in the register layout:
         // row r is value 4 (r / 8) + r % 4 of lane 32 ((r / 4) % 2) + column
